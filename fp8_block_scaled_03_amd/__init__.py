@@ -1,0 +1,19 @@
+"""FP8 (E4M3) GEMM with 32x32 block scales for AMD MI355X (gfx950).
+
+The compute path is the C-ABI library ``libfp8bs.so`` (HIP kernels); the
+functions exported here only marshal torch tensors into it.  Importing this
+package loads nothing; the first call loads the library and raises
+``Fp8bsError`` if it is missing.
+"""
+
+_BINDING_NAMES = ("Fp8bsError", "quantize", "gemm", "grouped_gemm", "library_path", "load_library",
+                  "quantize_raw", "gemm_raw", "grouped_gemm_raw")
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,113 @@
+/*
+ * fp8bs.h - C ABI of the FP8 (E4M3) GEMM with 32x32 block scales, for AMD
+ * MI355X (gfx950).
+ *
+ * Source pages cited below:
+ *   [DG]  the featured DeepGEMM FP8 write-up on hncyxsy.com (news item 241433)
+ *   [DET] "AI Infra 进阶：如何让大模型输出确定的结果" (aif.amtbbs.org, post 29992)
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers owned by the caller (the library
+ *     allocates nothing and keeps no state besides its code object).
+ *   - Matrices are dense row-major.  E4M3 means OCP E4M3FN bytes (bias 7, no
+ *     infinity, 0x7F/0xFF NaN, largest finite 448) [DG 2.1].  bf16 means the
+ *     upper 16 bits of an IEEE fp32.  Scale grids are row-major fp32.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously; nothing synchronizes.  Calls are reentrant.
+ *   - Argument checks happen on the host before any launch; a non-OK status
+ *     means nothing was enqueued (except FP8BS_EHIP, returned when the launch
+ *     itself failed).  No exception or abort crosses the ABI.
+ *   - Device-side preconditions that are NOT checked: inputs finite, scales
+ *     finite, outputs not aliasing inputs, buffers as large as stated.
+ *   - Results are batch invariant [DET part 一, sections 6-7]: an element of C
+ *     depends only on its row of A, its column of B and the scales, never on
+ *     M, on the row's position in the batch or on which kernel ran.  K is
+ *     never split; the 32-deep K-blocks are accumulated in ascending order.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BS_OK = 0,
+  FP8BS_EINVAL = 1, /* null pointer with a non-zero size, negative size, bad G  */
+  FP8BS_ESHAPE = 2, /* a dimension that must be a multiple of 32 is not, or a
+                       dimension is too large                                  */
+  FP8BS_EALIGN = 3, /* a matrix pointer not 16-byte aligned, or a scale/offset
+                       pointer not 4-byte aligned                              */
+  FP8BS_EHIP = 4,   /* the HIP runtime reported an error at launch              */
+  FP8BS_ENOSYS = 5  /* not built for this device                               */
+} fp8bs_status;
+
+/* Largest accepted group count for fp8bs_grouped_gemm. */
+#define FP8BS_MAX_GROUPS 1024
+
+/*
+ * fp8bs_quantize - bf16 -> E4M3 with one fp32 scale per 32x32 block.
+ *   [DG 2.2]: one scale per 32x32 block; [DG 5.2]: scale from the block's
+ *   absolute maximum; [DG 2.1]: E4M3 tops out at 448.
+ *   For block (rb, cb) covering rows [32rb, min(32rb+32, rows)) and columns
+ *   [32cb, 32cb+32):
+ *     amax = max |x| over the block;   s = amax / 448   (fp32, round to nearest)
+ *     s == 0:  every code of the block is 0x00
+ *     else:    q = E4M3(x / s), the quotient taken in fp32 (round to nearest)
+ *              and then rounded to E4M3 with ties to even, clamped to +-448,
+ *              sign kept (so -0 and negative underflow give 0x80).
+ *   x      [rows, cols]              bf16, 16-byte aligned
+ *   q      [rows, cols]              E4M3 out, 16-byte aligned
+ *   scales [ceil(rows/32), cols/32]  fp32 out, 4-byte aligned
+ *   cols % 32 == 0 (else FP8BS_ESHAPE); rows == 0 or cols == 0 is a no-op.
+ */
+fp8bs_status fp8bs_quantize(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
+                            void* stream);
+
+/*
+ * fp8bs_gemm - C = dequant(A) . dequant(B) with the scales folded in per
+ *   32-deep K-block [DG 2.2-2.3]:
+ *     C[i,j] = sum_kb  sa[i/32, kb] * sb[kb, j/32] * sum_{k in kb} A[i,k] B[k,j]
+ *   Each 32-deep partial is formed exactly from the decoded E4M3 values (fp32
+ *   result), multiplied by the fp32 product sa*sb and added into one fp32
+ *   accumulator, K-blocks in ascending order; C is rounded once to bf16
+ *   (nearest, ties to even).
+ *   a  [M, K] E4M3, 16-byte aligned      sa [ceil(M/32), K/32] fp32
+ *   b  [K, N] E4M3, 16-byte aligned      sb [K/32, N/32] fp32
+ *   c  [M, N] bf16 out, 16-byte aligned
+ *   K % 32 == 0 and N % 32 == 0 (else FP8BS_ESHAPE); M, N, K <= 2^30.
+ *   M == 0 or N == 0: no-op.  K == 0: C is filled with +0.
+ */
+fp8bs_status fp8bs_gemm(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16, int64_t M,
+                        int64_t N, int64_t K, void* stream);
+
+/*
+ * fp8bs_grouped_gemm - G independent GEMMs over consecutive row ranges of one
+ *   A, each with its own B_g [DG 4.1-4.2].  Row range g is
+ *   [offsets[g], offsets[g+1]); its rows are multiplied by b[g] with sb[g]
+ *   exactly as fp8bs_gemm would; empty ranges produce no work.  The offsets
+ *   live in DEVICE memory, so a captured graph stays valid when the group
+ *   sizes change [DG 4.3].
+ *   a       [M_total, K] E4M3          sa [M_total/32, K/32] fp32
+ *   b       [G, K, N] E4M3             sb [G, K/32, N/32] fp32
+ *   offsets [G+1] int32 on the device: 0 = off[0] <= off[1] <= ... <= off[G] = M_total,
+ *           every entry a multiple of 32.  Not checked on the host; the kernel
+ *           clamps each range into [0, M_total] and treats a decreasing range as
+ *           empty, so a bad table gives wrong rows, never an out-of-bounds access.
+ *   c       [M_total, N] bf16 out (rows outside every range are left untouched)
+ *   1 <= G <= FP8BS_MAX_GROUPS (else FP8BS_EINVAL); M_total, K, N multiples of 32.
+ */
+fp8bs_status fp8bs_grouped_gemm(const void* a, const float* sa, const void* b, const float* sb,
+                                const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
+                                int64_t K, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8bs_status_str(fp8bs_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */
