@@ -1,0 +1,81 @@
+// Shared device helpers for the gfx950 kernels of the E4M3 block-scaled GEMM.
+//
+// Numerics (identical in every kernel, so that results are batch invariant):
+//   * an E4M3 byte is decoded exactly to bf16 by the hardware converter
+//     (E4M3 values are a subset of bf16);
+//   * one 32-deep K-block partial P = sum_{k in block} a_k b_k is one
+//     v_mfma_f32_16x16x32_bf16 with a zero accumulator input (the bf16 MFMA
+//     forms the partial at full fp32 precision; the FP8 MFMA forms drop
+//     low-order product bits, which the accuracy bound does not allow);
+//   * promotion: s = sa * sb (fp32, one rounding), acc = fma(P, s, acc),
+//     K-blocks in ascending order into one fp32 accumulator
+//     (DeepGEMM write-up on hncyxsy.com, sections 2.2-2.3: the block scales
+//     enter during accumulation, not in a separate pass over C);
+//   * C = bf16(acc), round to nearest even, once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace fp8bs {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+typedef __attribute__((address_space(3))) v4s lds_v4s_t;
+typedef __attribute__((address_space(3))) v2i lds_v2i_t;
+
+// 4 E4M3 bytes (one dword) -> 4 bf16 (two dwords), exact.
+__device__ __forceinline__ v2i e4m3x4_to_bf16x4(uint32_t w) {
+  v2bf lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  v2bf hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return v2i{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+}
+
+// 8 E4M3 bytes -> the 8 bf16 operand of one MFMA lane.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16x8(v2i w) {
+  v2i lo = e4m3x4_to_bf16x4((uint32_t)w[0]);
+  v2i hi = e4m3x4_to_bf16x4((uint32_t)w[1]);
+  return __builtin_bit_cast(v8bf, v4i{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// 16 E4M3 bytes -> 16 bf16 (32 bytes).
+__device__ __forceinline__ void e4m3x16_to_bf16x16(uint4 w, uint4& out0, uint4& out1) {
+  v2i a = e4m3x4_to_bf16x4(w.x), b = e4m3x4_to_bf16x4(w.y);
+  v2i c = e4m3x4_to_bf16x4(w.z), d = e4m3x4_to_bf16x4(w.w);
+  out0 = make_uint4((uint32_t)a[0], (uint32_t)a[1], (uint32_t)b[0], (uint32_t)b[1]);
+  out1 = make_uint4((uint32_t)c[0], (uint32_t)c[1], (uint32_t)d[0], (uint32_t)d[1]);
+}
+
+// One 32-deep K-block partial for a 16x16 output sub-tile.
+__device__ __forceinline__ v4f mfma_partial(v8bf a, v8bf b) {
+  v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, z, 0, 0, 0);
+}
+
+// acc += P * s, element-wise, one rounding each.
+__device__ __forceinline__ void promote(v4f& acc, v4f p, float s) {
+  acc[0] = __builtin_fmaf(p[0], s, acc[0]);
+  acc[1] = __builtin_fmaf(p[1], s, acc[1]);
+  acc[2] = __builtin_fmaf(p[2], s, acc[2]);
+  acc[3] = __builtin_fmaf(p[3], s, acc[3]);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ int wave_id_uniform() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+}  // namespace fp8bs

@@ -1,0 +1,474 @@
+// E4M3 GEMM with 32x32 block scales for gfx950 (MI355X).
+//
+// C[i,j] = sum_kb sa[i/32,kb] * sb[kb,j/32] * sum_{k in kb} A[i,k] B[k,j]
+// (DeepGEMM write-up on hncyxsy.com, sections 2.2-2.3), every element computed
+// with the one recipe in common.hpp; K is never split across accumulators and
+// K-blocks are promoted in ascending order, so an element's bits do not depend
+// on M, on its position in the tile or on which kernel ran ("AI Infra 进阶：
+// 如何让大模型输出确定的结果", part 一 sections 6-7: batch invariance needs a
+// fixed reduction order, no M-dependent split-K).
+//
+// Two kernels:
+//  * tile kernel (large M, and the grouped variant): a 512-thread workgroup owns
+//    a 256x256 C tile; eight waves in a 4(M) x 2(N) grid own 64x128 each
+//    (4 x 8 MFMA sub-tiles of 16x16).  Per 32-deep K-block the workgroup
+//    loads 8 KB of A and 8 KB of B (16 bytes per thread each, coalesced),
+//    decodes E4M3 -> bf16 once, and stores the bf16 tiles into a double-buffered
+//    LDS ring with an XOR swizzle so that the fragment reads are free of bank
+//    conflicts (DeepGEMM write-up, section 3.1, makes the same point for shared
+//    memory; section 3.3 for overlapping the next tile's loads with compute).
+//    A fragments are read K-contiguous with ds_read_b128; B is N-contiguous in
+//    memory, so its fragments come from the LDS transpose read ds_read_b64_tr_b16.
+//  * small-M kernel (M <= 64, decode): a workgroup owns a 32-column slice of C
+//    for all rows and all of K.  Its eight waves each form the partials of
+//    different K-blocks (B streamed once from HBM, the op is bandwidth bound),
+//    pass them through LDS, and the promotion chain then runs in ascending
+//    K-block order - the same sequence of roundings as the tile kernel.
+#include "common.hpp"
+
+namespace fp8bs {
+
+// ------------------------------------------------------------------------------------
+// tile kernel
+// ------------------------------------------------------------------------------------
+constexpr int TBM = 256, TBN = 256, TTHREADS = 512;
+constexpr int A_STAGE_BYTES = TBM * 32 * 2;  // 16 KB bf16
+constexpr int B_STAGE_BYTES = 32 * TBN * 2;  // 16 KB bf16
+constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
+constexpr int TILE_LDS_BYTES = 2 * STAGE_BYTES;  // 64 KB
+
+// A tile in LDS: [256 rows][4 chunks of 8 bf16]; chunk c of row r lives at
+// position c ^ ((r >> 1) & 3).
+__device__ __forceinline__ int a_lds_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// B tile in LDS: [32 k][16 chunks of 16 bf16 (32 bytes)]; chunk j of row k lives at
+// position j ^ (k & 3).
+__device__ __forceinline__ int b_lds_off(int k, int chunk) { return k * 512 + ((chunk ^ (k & 3)) << 5); }
+
+struct TileArgs {
+  const uint8_t* a;   // rows of this problem start here (global row index 0)
+  const float* sa;    // [ceil(M/32), KB]
+  const uint8_t* b;   // [K, N]
+  const float* sb;    // [KB, NB]
+  uint16_t* c;        // [.., N]
+  int64_t N, K;
+  int64_t row0;       // first row of the tile
+  int64_t row_end;    // rows >= row_end are not part of this problem
+  int64_t col0;       // first column of the tile
+  int64_t sa_rows;    // number of scale rows (for clamping)
+};
+
+__device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = wave_id_uniform();
+  const int wm = w & 3, wn = w >> 2;
+  const int64_t K = p.K, N = p.N;
+  const int KB = (int)(K >> 5);
+  const int NB = (int)(N >> 5);
+
+  // ---- global -> register staging assignment
+  const int a_row = t >> 1, a_half = t & 1;           // 16 E4M3 of A row a_row
+  const int b_row = t >> 4, b_chunk = t & 15;         // 16 E4M3 of B row b_row
+  const int64_t ga_row = p.row0 + a_row;
+  const bool a_ok = ga_row < p.row_end;
+  const bool b_ok = (p.col0 + b_chunk * 16) < N;
+  const uint8_t* a_src = p.a + (a_ok ? ga_row : 0) * K + a_half * 16;
+  const uint8_t* b_src = p.b + (int64_t)b_row * N + (b_ok ? p.col0 + b_chunk * 16 : 0);
+
+  auto load_stage = [&](int kb, uint4& ra, uint4& rb) {
+    ra = a_ok ? *reinterpret_cast<const uint4*>(a_src + (int64_t)kb * 32) : make_uint4(0, 0, 0, 0);
+    rb = b_ok ? *reinterpret_cast<const uint4*>(b_src + (int64_t)kb * 32 * N) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_stage = [&](int stage, uint4 ra, uint4 rb) {
+    unsigned char* sA = smem + stage * STAGE_BYTES;
+    unsigned char* sB = sA + A_STAGE_BYTES;
+    uint4 a0, a1, b0, b1;
+    e4m3x16_to_bf16x16(ra, a0, a1);
+    e4m3x16_to_bf16x16(rb, b0, b1);
+    *reinterpret_cast<uint4*>(sA + a_lds_off(a_row, 2 * a_half)) = a0;
+    *reinterpret_cast<uint4*>(sA + a_lds_off(a_row, 2 * a_half + 1)) = a1;
+    unsigned char* bp = sB + b_lds_off(b_row, b_chunk);
+    *reinterpret_cast<uint4*>(bp) = b0;
+    *reinterpret_cast<uint4*>(bp + 16) = b1;
+  };
+
+  // ---- scale indices for this wave: 2 row-blocks x 4 column-blocks
+  int64_t rb0 = (p.row0 + wm * 64) >> 5;
+  int64_t rbs[2] = {rb0 < p.sa_rows ? rb0 : p.sa_rows - 1, rb0 + 1 < p.sa_rows ? rb0 + 1 : p.sa_rows - 1};
+  int cbs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int64_t cb = ((p.col0 + wn * 128) >> 5) + j;
+    cbs[j] = (int)(cb < NB ? cb : NB - 1);
+  }
+  const float* sa_r0 = p.sa + rbs[0] * KB;
+  const float* sa_r1 = p.sa + rbs[1] * KB;
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // fragment read offsets (relative to a stage)
+  const int fr_row_lo = lane & 15, fr_kc = lane >> 4;
+  const int tr_g = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
+
+  uint4 ra, rb;
+  if (KB > 0) {
+    load_stage(0, ra, rb);
+    store_stage(0, ra, rb);
+    if (KB > 1) load_stage(1, ra, rb);
+  }
+  __syncthreads();
+
+  for (int kb = 0; kb < KB; ++kb) {
+    const int cur = kb & 1;
+    const unsigned char* sA = smem + cur * STAGE_BYTES;
+    const unsigned char* sB = sA + A_STAGE_BYTES;
+
+    // scales for this K-block
+    float s_a0 = sa_r0[kb], s_a1 = sa_r1[kb];
+    float s_b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_b[j] = p.sb[(int64_t)kb * NB + cbs[j]];
+
+    // fragments
+    v8bf af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 64 + i * 16 + fr_row_lo;
+      af[i] = *reinterpret_cast<const v8bf*>(sA + a_lds_off(row, fr_kc));
+    }
+    v8bf bfrag[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int J = wn * 8 + j;
+      v4s h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s_t*)(sB + b_lds_off(8 * tr_g + tr_r, J) + tr_c * 8));
+      v4s h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s_t*)(sB + b_lds_off(8 * tr_g + 4 + tr_r, J) + tr_c * 8));
+      v2i x0 = __builtin_bit_cast(v2i, h0), x1 = __builtin_bit_cast(v2i, h1);
+      bfrag[j] = __builtin_bit_cast(v8bf, v4i{x0[0], x0[1], x1[0], x1[1]});
+    }
+
+    // stage the next K-block into the other buffer while this one is consumed
+    if (kb + 1 < KB) {
+      store_stage(cur ^ 1, ra, rb);
+      if (kb + 2 < KB) load_stage(kb + 2, ra, rb);
+    }
+
+    float s[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s[0][j] = s_a0 * s_b[j];
+      s[1][j] = s_a1 * s_b[j];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) promote(acc[i][j], mfma_partial(af[i], bfrag[j]), s[i >> 1][j >> 1]);
+
+    __syncthreads();
+  }
+
+  // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
+  // 16-byte coalesced global stores
+  unsigned char* ep = smem + w * (32 * 128 * 2);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = pass * 2 + ii;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = ii * 16 + 4 * (lane >> 4) + r;
+          const int lc = j * 16 + (lane & 15);
+          *reinterpret_cast<uint16_t*>(ep + lr * 256 + lc * 2) = (uint16_t)bf16_rne(acc[i][j][r]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int lr = it * 4 + (lane >> 4);
+      const int lc = (lane & 15) * 8;
+      uint4 v = *reinterpret_cast<const uint4*>(ep + lr * 256 + lc * 2);
+      const int64_t grow = p.row0 + wm * 64 + pass * 32 + lr;
+      const int64_t gcol = p.col0 + wn * 128 + lc;
+      if (grow < p.row_end && gcol < N) *reinterpret_cast<uint4*>(p.c + grow * N + gcol) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Tile order: consecutive workgroup ids are dealt round-robin to the 8 XCDs, so
+// ids are first re-dealt so that each XCD sees a contiguous run of tiles; the
+// run is walked in groups of 4 M-tiles so that neighbours share A rows and B
+// columns in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int64_t id, int64_t n_tiles, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  const int64_t per_xcd = (n_tiles + 7) / 8;
+  const int64_t lin = (id & 7) * per_xcd + (id >> 3);  // callers remap only when n_tiles % 8 == 0
+  const int64_t GM = 4;
+  const int64_t group = lin / (GM * tiles_n);
+  const int64_t first_m = group * GM;
+  const int64_t tiles_m_total = (n_tiles / tiles_n);
+  const int64_t gm = (tiles_m_total - first_m) < GM ? (tiles_m_total - first_m) : GM;
+  const int64_t r = lin - group * GM * tiles_n;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+__global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __restrict__ a,
+                                                             const float* __restrict__ sa,
+                                                             const uint8_t* __restrict__ b,
+                                                             const float* __restrict__ sb, uint16_t* __restrict__ c,
+                                                             int64_t M, int64_t N, int64_t K, int64_t tiles_m,
+                                                             int64_t tiles_n, int remap) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t n_tiles = tiles_m * tiles_n;
+  int64_t tm, tn;
+  if (remap) {
+    tile_coords(blockIdx.x, n_tiles, tiles_n, tm, tn);
+  } else {
+    tm = blockIdx.x / tiles_n;
+    tn = blockIdx.x % tiles_n;
+  }
+  TileArgs p;
+  p.a = a;
+  p.sa = sa;
+  p.b = b;
+  p.sb = sb;
+  p.c = c;
+  p.N = N;
+  p.K = K;
+  p.row0 = tm * TBM;
+  p.row_end = M;
+  p.col0 = tn * TBN;
+  p.sa_rows = (M + 31) >> 5;
+  tile_body(p, smem);
+}
+
+// Grouped: the grid is an upper bound on the tile count, (M_total/256 + G) x
+// tiles_n; each workgroup walks the device-side offsets to find its group and
+// M-tile, and leaves if it has none.  Shapes never enter launch arguments that
+// change with the group sizes (DeepGEMM write-up, section 4.3).
+__global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* __restrict__ a,
+                                                                const float* __restrict__ sa,
+                                                                const uint8_t* __restrict__ b,
+                                                                const float* __restrict__ sb,
+                                                                const int32_t* __restrict__ offsets, int G,
+                                                                uint16_t* __restrict__ c, int64_t M_total, int64_t N,
+                                                                int64_t K, int64_t tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t tn = blockIdx.x % tiles_n;
+  int64_t tm_lin = blockIdx.x / tiles_n;
+  // walk the groups (uniform across the workgroup)
+  int g = 0;
+  int64_t start = 0, end = 0;
+  bool found = false;
+  int64_t prev_end = 0;
+  for (g = 0; g < G; ++g) {
+    int64_t s0 = offsets[g], s1 = offsets[g + 1];
+    s0 = s0 < 0 ? 0 : (s0 > M_total ? M_total : s0);
+    s1 = s1 < 0 ? 0 : (s1 > M_total ? M_total : s1);
+    if (s0 < prev_end) s0 = prev_end;  // overlapping ranges are clipped
+    if (s1 < s0) s1 = s0;
+    prev_end = s1;
+    const int64_t mt = (s1 - s0 + TBM - 1) / TBM;
+    if (tm_lin < mt) {
+      start = s0 + tm_lin * TBM;
+      end = s1;
+      found = true;
+      break;
+    }
+    tm_lin -= mt;
+  }
+  if (!found) return;
+  const int64_t KB = K >> 5, NB = N >> 5;
+  TileArgs p;
+  p.a = a;
+  p.sa = sa;
+  p.b = b + (int64_t)g * K * N;
+  p.sb = sb + (int64_t)g * KB * NB;
+  p.c = c;
+  p.N = N;
+  p.K = K;
+  p.row0 = start;
+  p.row_end = end;
+  p.col0 = tn * TBN;
+  p.sa_rows = M_total >> 5;
+  tile_body(p, smem);
+}
+
+// ------------------------------------------------------------------------------------
+// small-M kernel
+// ------------------------------------------------------------------------------------
+constexpr int SBN = 32;          // columns per workgroup
+constexpr int SWAVES = 8;        // K-blocks formed per round (one per wave)
+constexpr int STHREADS = SWAVES * 64;
+
+// Per-wave B staging (E4M3, 32 k x 32 bytes) with the two 16-byte halves of
+// row k swapped when bit 2 of k is set, which makes the transposed reads free
+// of bank conflicts.
+__device__ __forceinline__ int sb_lds_off(int k, int half) { return k * 32 + ((half ^ ((k >> 2) & 1)) << 4); }
+
+template <int MT>  // number of 16-row MFMA sub-tiles (M <= 16 * MT)
+__global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __restrict__ a,
+                                                               const float* __restrict__ sa,
+                                                               const uint8_t* __restrict__ b,
+                                                               const float* __restrict__ sb,
+                                                               uint16_t* __restrict__ c, int64_t M, int64_t N,
+                                                               int64_t K) {
+  // LDS: B staging [8 waves][1 KB], partials [8 waves][MT][2][64 lanes] v4f
+  __shared__ __attribute__((aligned(16))) unsigned char s_b[SWAVES][1024];
+  __shared__ v4f s_p[SWAVES][MT * 2 * 64];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = wave_id_uniform();
+  const int KB = (int)(K >> 5), NB = (int)(N >> 5);
+  // XCD-aware: workgroups on one XCD take adjacent column slices so the 128-byte
+  // lines of B they share are fetched into that XCD's L2 once.
+  const int64_t n_slices = N / SBN;
+  const int64_t id = blockIdx.x;
+  const int64_t slice = (n_slices & 7) ? id : (id & 7) * (n_slices >> 3) + (id >> 3);
+  const int64_t n0 = slice * SBN;
+  const int cb = (int)(n0 >> 5);
+
+  // this wave's B load: row (lane >> 1), 16-byte half (lane & 1)
+  const int bl_k = lane >> 1, bl_h = lane & 1;
+  const uint8_t* b_src = b + (int64_t)bl_k * N + n0 + bl_h * 16;
+  // A fragment rows for this lane
+  const int a_kc = lane >> 4;
+
+  // chain ownership: thread t promotes (i, j, lane) = decode(t) when t < MT*2*64
+  const int ch_i = t / 128, ch_j = (t >> 6) & 1, ch_l = t & 63;
+  const bool ch_active = t < MT * 2 * 64;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int rounds = (KB + SWAVES - 1) / SWAVES;
+  uint4 rb_next = make_uint4(0, 0, 0, 0);
+  v2i ra_next[MT];
+  auto load = [&](int kb, uint4& rbv, v2i* rav) {
+    if (kb < KB) {
+      rbv = *reinterpret_cast<const uint4*>(b_src + (int64_t)kb * 32 * N);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int64_t row = i * 16 + (lane & 15);
+        rav[i] = row < M ? *reinterpret_cast<const v2i*>(a + row * K + (int64_t)kb * 32 + a_kc * 8) : v2i{0, 0};
+      }
+    }
+  };
+  load(w, rb_next, ra_next);
+
+  for (int r = 0; r < rounds; ++r) {
+    const int kb = r * SWAVES + w;
+    uint4 rbv = rb_next;
+    v2i rav[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) rav[i] = ra_next[i];
+    load(kb + SWAVES, rb_next, ra_next);  // prefetch the next round
+
+    if (kb < KB) {
+      // B tile -> LDS (wave-private), then transposed 8-byte reads
+      *reinterpret_cast<uint4*>(&s_b[w][sb_lds_off(bl_k, bl_h)]) = rbv;
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_wave_barrier();
+      v8bf bfrag[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int L = lane & 15;
+        const int k = 8 * (lane >> 4) + (L >> 1);
+        v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)&s_b[w][sb_lds_off(k, j) + 8 * (L & 1)]);
+        bfrag[j] = e4m3x8_to_bf16x8(x);
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        v8bf af = e4m3x8_to_bf16x8(rav[i]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s_p[w][(i * 2 + j) * 64 + lane] = mfma_partial(af, bfrag[j]);
+      }
+    }
+    __syncthreads();
+    if (ch_active) {
+      const int nkb = (KB - r * SWAVES) < SWAVES ? (KB - r * SWAVES) : SWAVES;
+      const int64_t rbk = (ch_i * 16) >> 5;  // row-block of this sub-tile
+      for (int q = 0; q < nkb; ++q) {
+        const int kbq = r * SWAVES + q;
+        const float s = sa[rbk * KB + kbq] * sb[(int64_t)kbq * NB + cb];
+        promote(acc, s_p[q][(ch_i * 2 + ch_j) * 64 + ch_l], s);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (ch_active) {
+    const int col = (int)n0 + ch_j * 16 + (ch_l & 15);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int64_t row = ch_i * 16 + 4 * (ch_l >> 4) + rr;
+      if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[rr]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------
+hipError_t launch_gemm_tile(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + TBN - 1) / TBN;
+  const int64_t n_tiles = tiles_m * tiles_n;
+  const int remap = (n_tiles % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(gemm_tile_kernel, dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                     (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped(const void* a, const float* sa, const void* b, const float* sb,
+                               const int32_t* offsets, int G, void* c, int64_t M_total, int64_t N, int64_t K,
+                               hipStream_t stream) {
+  const int64_t tiles_n = (N + TBN - 1) / TBN;
+  const int64_t tiles_m_max = M_total / TBM + G;  // sum over groups of ceil(M_g / 256)
+  const int64_t grid = tiles_m_max * tiles_n;
+  hipLaunchKernelGGL(gemm_grouped_kernel, dim3((unsigned)grid), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                     (const uint8_t*)a, sa, (const uint8_t*)b, sb, offsets, G, (uint16_t*)c, M_total, N, K, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_smallm(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t grid = N / SBN;
+  const int mt = (int)((M + 15) / 16);
+  switch (mt) {
+    case 1:
+      hipLaunchKernelGGL(gemm_smallm_kernel<1>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
+                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
+      break;
+    case 2:
+      hipLaunchKernelGGL(gemm_smallm_kernel<2>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
+                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
+      break;
+    case 3:
+      hipLaunchKernelGGL(gemm_smallm_kernel<3>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
+                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
+      break;
+    default:
+      hipLaunchKernelGGL(gemm_smallm_kernel<4>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
+                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t set_gemm_attributes() {
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_tile_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     TILE_LDS_BYTES);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             TILE_LDS_BYTES);
+}
+
+}  // namespace fp8bs

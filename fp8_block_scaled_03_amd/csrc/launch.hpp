@@ -1,0 +1,20 @@
+// Internal launcher declarations (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, void* q, float* scales, hipStream_t stream);
+hipError_t launch_gemm_tile(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
+                            int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_smallm(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_grouped(const void* a, const float* sa, const void* b, const float* sb,
+                               const int32_t* offsets, int G, void* c, int64_t M_total, int64_t N, int64_t K,
+                               hipStream_t stream);
+hipError_t set_gemm_attributes();
+
+// M at or below which the bandwidth-oriented small-M kernel runs.  Both kernels
+// follow the same per-element recipe, so the switch never changes a result.
+constexpr int64_t SMALL_M_MAX = 64;
+}  // namespace fp8bs

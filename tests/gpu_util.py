@@ -1,0 +1,64 @@
+"""Helpers for the GPU tests: move numpy inputs to the device, call the
+library through the binding, bring results back as numpy bit patterns."""
+
+import sys
+
+import numpy as np
+import torch
+
+import fp8_block_scaled_03_amd as fp8bs
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    """Name the case before each GPU step (stdout, flushed)."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.to(DEV).view(torch.bfloat16)
+
+
+def u8_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to(DEV)
+
+
+def f32_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def i32_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(DEV)
+
+
+def bits_np(t):
+    """bf16 device tensor -> uint16 numpy bit patterns."""
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_quantize(x_bits):
+    q, s = fp8bs.quantize(bf16_dev(x_bits))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def gpu_gemm(qa, sa, qb, sb):
+    c = fp8bs.gemm(u8_dev(qa), f32_dev(sa), u8_dev(qb), f32_dev(sb))
+    torch.cuda.synchronize()
+    return bits_np(c)
+
+
+def gpu_grouped(qa, sa, qb, sb, offsets, c_init=None):
+    out = None
+    if c_init is not None:
+        out = bf16_dev(c_init)
+    c = fp8bs.grouped_gemm(u8_dev(qa), f32_dev(sa), u8_dev(qb), f32_dev(sb), i32_dev(offsets), out=out)
+    torch.cuda.synchronize()
+    return bits_np(c)
+
+
+def bits_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,178 @@
+"""GEMM parity against the oracle, exact special cases, and batch invariance."""
+
+import numpy as np
+import pytest
+
+import oracle
+from fp8_block_scaled_03_amd import workloads as W
+
+from gpu_util import bits_to_f64, gpu_gemm, gpu_grouped, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand_codes(g, shape):
+    return oracle.FINITE_E4M3_CODES[g.integers(0, len(oracle.FINITE_E4M3_CODES), shape)]
+
+
+def _rand_scales(g, shape):
+    return (g.uniform(1.0, 2.0, shape) * np.exp2(g.integers(-10, 4, shape))).astype(np.float32)
+
+
+def _quantized(seed, rows, cols, std=1.0, outlier=0.0):
+    return oracle.quantize_blocks(W.normal_bf16(seed, 0, rows, cols, std, outlier))
+
+
+def _assert_tol(c_bits, ref, absref, label):
+    c = bits_to_f64(c_bits)
+    ok = oracle.tolerance_ok(c, ref, absref)
+    bad = np.argwhere(~ok)
+    assert len(bad) == 0, (f"{label}: {len(bad)} of {ok.size} outside the bound; first {bad[:4].tolist()}, "
+                           f"worst ratio {np.max(np.abs(c - ref) / oracle.tolerance_bound(ref, absref)):.3g}")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (256, 256, 256),      # square-256 shape, tile kernel
+    (300, 96, 96),        # ragged M and N (N < tile), several K-blocks
+    (520, 288, 160),      # three M-tiles, two N-tiles, ragged tails
+    (1, 64, 256), (8, 96, 128), (33, 32, 64), (64, 160, 96),   # small-M kernel
+    (65, 64, 64),         # just above the small-M limit
+])
+def test_gemm_matches_oracle(M, N, K):
+    qa, sa = _quantized(2000 + M, M, K)
+    qb, sb = _quantized(3000 + N, K, N, std=0.02)
+    say(f"gemm M={M} N={N} K={K}")
+    c = gpu_gemm(qa, sa, qb, sb)
+    ref, absref = oracle.gemm_ref(qa, sa, qb, sb)
+    _assert_tol(c, ref, absref, f"M={M} N={N} K={K}")
+
+
+def test_square_256_workload():
+    wl = W.square_256()
+    qa, sa = oracle.quantize_blocks(wl.a_bits())
+    qb, sb = oracle.quantize_blocks(wl.b_bits())
+    say("gemm square-256 workload")
+    c = gpu_gemm(qa, sa, qb, sb)
+    ref, absref = oracle.gemm_ref(qa, sa, qb, sb)
+    _assert_tol(c, ref, absref, "square-256")
+
+
+@pytest.mark.parametrize("M", [1, 40, 300])
+def test_random_codes_and_scales(M):
+    """Arbitrary finite codes (subnormals included) and non-power-of-two scales."""
+    g = np.random.default_rng(M)
+    K, N = 128, 64
+    qa, qb = _rand_codes(g, (M, K)), _rand_codes(g, (K, N))
+    sa, sb = _rand_scales(g, (-(-M // 32), K // 32)), _rand_scales(g, (K // 32, N // 32))
+    say(f"gemm random codes M={M}")
+    c = gpu_gemm(qa, sa, qb, sb)
+    ref, absref = oracle.gemm_ref(qa, sa, qb, sb)
+    _assert_tol(c, ref, absref, f"random codes M={M}")
+
+
+@pytest.mark.parametrize("M", [64, 256])
+def test_identity_is_exact(M):
+    """A = I (code 0x38) with unit scales: C = bf16(dec(B)) bit for bit (E4M3 is a
+    subset of bf16).  Pins operand decode, the B layout and OCP E4M3."""
+    g = np.random.default_rng(11)
+    K = M
+    N = 96
+    qa = np.zeros((M, K), np.uint8)
+    qa[np.arange(M), np.arange(M)] = 0x38
+    qb = _rand_codes(g, (K, N))
+    say(f"gemm identity M={M}")
+    c = gpu_gemm(qa, np.ones((M // 32, K // 32), np.float32), qb, np.ones((K // 32, N // 32), np.float32))
+    expect = W.f32_to_bf16_bits(oracle.decode_e4m3(qb).astype(np.float32))
+    expect[expect == 0x8000] = 0          # -0 * 1 + (+0 products) sums to +0
+    assert np.array_equal(c, expect)
+
+
+def test_power_of_two_scales_commute_bitwise():
+    qa, sa = _quantized(21, 96, 128)
+    qb, sb = _quantized(22, 128, 64, std=0.02)
+    say("gemm power-of-two scaling")
+    c0 = gpu_gemm(qa, sa, qb, sb)
+    c1 = gpu_gemm(qa, sa * np.float32(2.0 ** 5), qb, sb * np.float32(2.0 ** -2))
+    assert np.array_equal(bits_to_f64(c1), bits_to_f64(c0) * 8.0)
+
+
+def test_zero_blocks_and_empty_k():
+    qa, sa = _quantized(23, 80, 64)
+    qb, sb = _quantized(24, 64, 64, std=0.02)
+    sa[:, 0] = 0.0
+    qb[32:, :] = 0
+    say("gemm zero blocks")
+    c = gpu_gemm(qa, sa, qb, sb)
+    assert np.all(c == 0)
+    say("gemm K=0")
+    c = gpu_gemm(np.zeros((70, 0), np.uint8), np.zeros((3, 0), np.float32), np.zeros((0, 64), np.uint8),
+                 np.zeros((0, 2), np.float32))
+    assert np.all(c == 0)
+
+
+def test_rows_independent_of_batch():
+    """Row i of C is bitwise the same computed alone (M=1, small-M kernel),
+    inside M=64 (small-M kernel) and inside M=320 (tile kernel)."""
+    qa, sa = _quantized(25, 320, 256)
+    qb, sb = _quantized(26, 256, 96, std=0.02)
+    say("invariance full M=320")
+    full = gpu_gemm(qa, sa, qb, sb)
+    say("invariance M=64")
+    part = gpu_gemm(qa[:64], sa[:2], qb, sb)
+    assert np.array_equal(part, full[:64])
+    for i in (0, 5, 31, 32, 63, 64, 100, 255, 319):
+        say(f"invariance row {i}")
+        one = gpu_gemm(qa[i:i + 1], sa[i // 32:i // 32 + 1], qb, sb)
+        assert np.array_equal(one[0], full[i]), f"row {i}"
+    for m in (1, 8, 32):
+        say(f"invariance prefix M={m}")
+        pre = gpu_gemm(qa[:m], sa[:-(-m // 32)], qb, sb)
+        assert np.array_equal(pre, full[:m])
+
+
+def test_row_blocks_permute_and_repeat():
+    qa, sa = _quantized(27, 512, 128)
+    qb, sb = _quantized(28, 128, 64, std=0.02)
+    say("permutation base")
+    c = gpu_gemm(qa, sa, qb, sb)
+    perm = np.random.default_rng(0).permutation(16)
+    rows = (perm[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    say("permutation permuted")
+    cp = gpu_gemm(qa[rows], sa[perm], qb, sb)
+    assert np.array_equal(cp, c[rows])
+    for _ in range(2):
+        assert np.array_equal(gpu_gemm(qa, sa, qb, sb), c)
+
+
+def test_grouped_matches_oracle_and_single_gemm():
+    g = np.random.default_rng(31)
+    G, K, N = 6, 128, 96
+    rows = np.array([64, 0, 288, 32, 0, 96])
+    off = W.offsets_from_rows(rows)
+    M = int(off[-1])
+    qa, sa = _quantized(32, M, K)
+    qb = np.stack([_quantized(40 + i, K, N, std=0.02)[0] for i in range(G)])
+    sb = np.stack([_quantized(40 + i, K, N, std=0.02)[1] for i in range(G)])
+    say("grouped small")
+    c = gpu_grouped(qa, sa, qb, sb, off)
+    ref, absref = oracle.grouped_gemm_ref(qa, sa, qb, sb, off)
+    _assert_tol(c, ref, absref, "grouped")
+    for gi in range(G):
+        r0, r1 = off[gi], off[gi + 1]
+        if r1 > r0:
+            say(f"grouped vs single group {gi}")
+            single = gpu_gemm(qa[r0:r1], sa[r0 // 32:r1 // 32], qb[gi], sb[gi])
+            assert np.array_equal(single, c[r0:r1])
+    del g
+
+
+def test_grouped_all_empty_but_one_and_untouched_rows():
+    K, N = 64, 64
+    off = np.array([0, 0, 64, 64], np.int32)
+    qa, sa = _quantized(50, 64, K)
+    qb = np.stack([_quantized(51 + i, K, N)[0] for i in range(3)])
+    sb = np.stack([_quantized(51 + i, K, N)[1] for i in range(3)])
+    say("grouped one live group")
+    c = gpu_grouped(qa, sa, qb, sb, off)
+    ref, absref = oracle.grouped_gemm_ref(qa, sa, qb, sb, off)
+    _assert_tol(c, ref, absref, "grouped one live group")
