@@ -1,0 +1,253 @@
+"""Benchmark of the E4M3 block-scaled GEMM hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: quantize the bf16
+activations A and weights B to E4M3 with 32x32 block scales, then the
+block-scaled GEMM to bf16 C, on the square 4096 x 4096 x 4096 workload (inputs
+N(0,1), seeded, already resident in HBM).  `value` is 2*M*N*K per step over the
+measured step time (TFLOP/s of the whole path).
+
+Also measured (same run, reported under "detail"):
+  * the GEMM kernel alone, per launch with HIP events on the launch stream, with
+    the caches flushed before each launch (a 1 GiB fill), and its roofline
+    against MI355X's dense FP8 MFMA peak;
+  * the small-M (decode) GEMM at K=8192, M in {1, 8, 32, 64}, N in
+    {8192, 28672}: algorithmic HBM bytes per launch over the kernel time;
+  * the quantizer alone (HBM bytes per launch over its time);
+  * the CPU oracle on a bounded sample of the same workload ("cpu_baseline").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+       python bench.py --profile-kernels   (a short run for rocprofv3 passes)
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
+BF16_DENSE_PEAK_TFLOPS = 2500.0
+METRIC = "FP8 block-scaled GEMM TFLOPS & % MFMA peak @4096³; small-M HBM GB/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tile_square4096.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--reps", type=int, default=50, help="per-kernel timed launches (flushed)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--quick", action="store_true", help="fewer reps, no decode sweep (for profiling)")
+    p.add_argument("--profile-kernels", action="store_true",
+                   help="run each kernel a few times without timing (for rocprofv3 counter passes)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU mode (it shards along M or N "
+              "with no exchange, so one GPU's share is the measured unit); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_block_scaled_03_amd as fp8bs
+    from fp8_block_scaled_03_amd import workloads as W
+
+    fp8bs.load_library()  # fail loudly before any work if the library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def flush():
+        flush_buf.fill_(1)  # 1 GiB of writes evicts L2 and the 256 MB Infinity Cache
+
+    def time_launch(fn, reps, do_flush=True):
+        """Median and min per-launch time in ms, HIP events on the launch stream."""
+        times = []
+        for _ in range(reps):
+            if do_flush:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        return times[len(times) // 2], times[0], sum(times) / len(times)
+
+    # ---- headline workload: square 4096^3
+    wl = W.square_4096()
+    M, N, K = wl.M, wl.N, wl.K
+    a = to_dev_bf16(wl.a_bits())
+    b = to_dev_bf16(wl.b_bits())
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qb = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M // 32, K // 32), dtype=torch.float32, device=dev)
+    sb = torch.empty((K // 32, N // 32), dtype=torch.float32, device=dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        fp8bs.quantize(a, qa, sa)
+        fp8bs.quantize(b, qb, sb)
+        fp8bs.gemm(qa, sa, qb, sb, out=c)
+
+    def gemm_only():
+        fp8bs.gemm(qa, sa, qb, sb, out=c)
+
+    if args.profile_kernels:
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        # one decode shape so its kernel shows up too
+        dwl = W.decode(8, 8192)
+        da = to_dev_bf16(dwl.a_bits())
+        db = to_dev_bf16(dwl.b_bits())
+        dqa, dsa = fp8bs.quantize(da)
+        dqb, dsb = fp8bs.quantize(db)
+        for _ in range(3):
+            fp8bs.gemm(dqa, dsa, dqb, dsb)
+        # plain copy of known size, for scaling the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernels": "done", "copy_bytes": 256 << 20}))
+        return
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    value = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
+
+    reps = 10 if args.quick else args.reps
+    for _ in range(5):
+        gemm_only()
+    g_med, g_min, g_avg = time_launch(gemm_only, reps)
+    q_med, q_min, q_avg = time_launch(lambda: fp8bs.quantize(a, qa, sa), reps)
+    gemm_flops = 2.0 * M * N * K
+    # algorithmic bytes of one GEMM launch: A + B (E4M3) + both scale grids + C (bf16)
+    gemm_bytes = M * K + K * N + 4 * (M // 32) * (K // 32) + 4 * (K // 32) * (N // 32) + 2 * M * N
+    achieved = gemm_flops / (g_avg * 1e-3) / 1e12
+
+    # HBM bytes per launch from the committed rocprofv3 counter summary, only
+    # while the GEMM sources are the ones that were profiled
+    from fp8_block_scaled_03_amd import profiling
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = profiling.read_traffic(TRAFFIC_FILE)
+        if tr.get("source_sha") == profiling.source_sha():
+            traffic = int(float(tr["hbm_bytes_per_launch"]))
+
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": "gemm_tile_kernel", "per_launch_flops": gemm_flops, "per_launch_alg_bytes": gemm_bytes,
+                "avg_ms": round(g_avg, 5)}
+
+    detail = {
+        "gemm_kernel_ms": {"median": round(g_med, 5), "min": round(g_min, 5), "mean": round(g_avg, 5)},
+        "gemm_kernel_tflops_median": round(gemm_flops / (g_med * 1e-3) / 1e12, 1),
+        "gemm_frac_of_bf16_mfma_peak": round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
+        "quantize_4096x4096_ms_median": round(q_med, 5),
+        "quantize_4096x4096_gbs": round(3.0 * M * K / (q_med * 1e-3) / 1e9, 1),
+    }
+
+    if not args.quick:
+        decode = []
+        for n_dec in (8192, 28672):
+            dwl = W.decode(64, n_dec)
+            a64 = to_dev_bf16(dwl.a_bits())
+            db = to_dev_bf16(dwl.b_bits())
+            q64, s64 = fp8bs.quantize(a64)
+            dqb, dsb = fp8bs.quantize(db)
+            for m in (1, 8, 32, 64):
+                dqa, dsa = q64[:m].contiguous(), s64[:(m + 31) // 32].contiguous()
+                dc = torch.empty((m, n_dec), dtype=torch.bfloat16, device=dev)
+                fn = (lambda dqa=dqa, dsa=dsa, dc=dc: fp8bs.gemm(dqa, dsa, dqb, dsb, out=dc))
+                for _ in range(3):
+                    fn()
+                d_med, d_min, d_avg = time_launch(fn, reps)
+                nbytes = m * dwl.K + dwl.K * n_dec + 4 * ((m + 31) // 32) * (dwl.K // 32) \
+                    + 4 * (dwl.K // 32) * (n_dec // 32) + 2 * m * n_dec
+                decode.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
+                               "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            del a64, db, q64, s64, dqb, dsb
+        detail["decode_small_m"] = decode
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (exact bf16 MFMA products, fp32 accumulation)",
+        "data": "synthetic",
+        "config": {"workload": "square-4096: quantize A, B (bf16 -> E4M3, 32x32 scales) + block-scaled GEMM",
+                   "M": M, "N": N, "K": K, "block": 32, "seed": wl.seed},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl):
+    """The oracle, as it stands, on a bounded sample of the square-4096 step:
+    quantize all of B and the first `rows` rows of A, then the fp64 reference for
+    those rows x all columns.  Throughput is that sample's 2*rows*N*K over its
+    wall time."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    rows = 4096
+    a_bits = wl.a_bits()[:rows]
+    b_bits = wl.b_bits()
+    t0 = time.perf_counter()
+    qa, sa = oracle.quantize_blocks(a_bits)
+    qb, sb = oracle.quantize_blocks(b_bits)
+    oracle.gemm_ref(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(2.0 * rows * wl.N * wl.K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"square-4096 step restricted to A rows 0..{rows - 1}: oracle quantize (A rows, all of B) "
+                      f"+ fp64 reference GEMM {rows}x{wl.N}x{wl.K}",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()
