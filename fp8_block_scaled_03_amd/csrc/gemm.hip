@@ -33,16 +33,25 @@ namespace fp8bs {
 // ------------------------------------------------------------------------------------
 constexpr int TBM = 256, TBN = 256, TTHREADS = 512;
 constexpr int A_STAGE_BYTES = TBM * 32 * 2;  // 16 KB bf16
-constexpr int B_STAGE_BYTES = 32 * TBN * 2;  // 16 KB bf16
+constexpr int B_STAGE_BYTES = 32 * TBN * 2 + 512;  // 16 KB bf16 + row-group shifts
 constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
-constexpr int TILE_LDS_BYTES = 2 * STAGE_BYTES;  // 64 KB
+constexpr int TILE_STAGES = 3;
+// Scales are staged in LDS in windows of SCW K-blocks (double-buffered): per
+// window 8 row-blocks of sa and 8 column-blocks of sb.
+constexpr int SCW = 128;
+constexpr int SC_WINDOW_BYTES = 2 * 8 * SCW * 4;  // 8 KB
+constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + 2 * SC_WINDOW_BYTES;  // 112 KB
 
 // A tile in LDS: [256 rows][4 chunks of 8 bf16]; chunk c of row r lives at
 // position c ^ ((r >> 1) & 3).
 __device__ __forceinline__ int a_lds_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 // B tile in LDS: [32 k][16 chunks of 16 bf16 (32 bytes)]; chunk j of row k lives at
-// position j ^ (k & 3).
-__device__ __forceinline__ int b_lds_off(int k, int chunk) { return k * 512 + ((chunk ^ (k & 3)) << 5); }
+// position j ^ (k & 3), and each group of 8 rows is shifted by a further 128
+// bytes: one transposed read touches rows k and k+8 together, and the shift
+// puts them in different banks.
+__device__ __forceinline__ int b_lds_off(int k, int chunk) {
+  return k * 512 + (k >> 3) * 128 + ((chunk ^ (k & 3)) << 5);
+}
 
 struct TileArgs {
   const uint8_t* a;   // rows of this problem start here (global row index 0)
@@ -65,6 +74,9 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   const int64_t K = p.K, N = p.N;
   const int KB = (int)(K >> 5);
   const int NB = (int)(N >> 5);
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  lds_u8* const sA = (lds_u8*)smem;                            // 3 A stages
+  lds_u8* const sB = sA + TILE_STAGES * A_STAGE_BYTES;         // 3 B stages
 
   // ---- global -> register staging assignment
   const int a_row = t >> 1, a_half = t & 1;           // 16 E4M3 of A row a_row
@@ -74,35 +86,90 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   const bool b_ok = (p.col0 + b_chunk * 16) < N;
   const uint8_t* a_src = p.a + (a_ok ? ga_row : 0) * K + a_half * 16;
   const uint8_t* b_src = p.b + (int64_t)b_row * N + (b_ok ? p.col0 + b_chunk * 16 : 0);
+  // LDS store addresses (stage 0); other stages add a compile-time offset
+  lds_u8* const st_a0 = sA + a_lds_off(a_row, 2 * a_half);
+  lds_u8* const st_a1 = sA + a_lds_off(a_row, 2 * a_half + 1);
+  lds_u8* const st_b = sB + b_lds_off(b_row, b_chunk);
 
-  auto load_stage = [&](int kb, uint4& ra, uint4& rb) {
+  auto load_stage = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
     ra = a_ok ? *reinterpret_cast<const uint4*>(a_src + (int64_t)kb * 32) : make_uint4(0, 0, 0, 0);
     rb = b_ok ? *reinterpret_cast<const uint4*>(b_src + (int64_t)kb * 32 * N) : make_uint4(0, 0, 0, 0);
   };
-  auto store_stage = [&](int stage, uint4 ra, uint4 rb) {
-    unsigned char* sA = smem + stage * STAGE_BYTES;
-    unsigned char* sB = sA + A_STAGE_BYTES;
+  // `st` is the stage index (wave-uniform, 0..2)
+  auto store_stage = [&](int st, uint4 ra, uint4 rb) __attribute__((always_inline)) {
     uint4 a0, a1, b0, b1;
     e4m3x16_to_bf16x16(ra, a0, a1);
     e4m3x16_to_bf16x16(rb, b0, b1);
-    *reinterpret_cast<uint4*>(sA + a_lds_off(a_row, 2 * a_half)) = a0;
-    *reinterpret_cast<uint4*>(sA + a_lds_off(a_row, 2 * a_half + 1)) = a1;
-    unsigned char* bp = sB + b_lds_off(b_row, b_chunk);
-    *reinterpret_cast<uint4*>(bp) = b0;
-    *reinterpret_cast<uint4*>(bp + 16) = b1;
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4u lds_v4u;
+    const int soa = st * A_STAGE_BYTES, sob = st * B_STAGE_BYTES;
+    *(lds_v4u*)(st_a0 + soa) = v4u{a0.x, a0.y, a0.z, a0.w};
+    *(lds_v4u*)(st_a1 + soa) = v4u{a1.x, a1.y, a1.z, a1.w};
+    *(lds_v4u*)(st_b + sob) = v4u{b0.x, b0.y, b0.z, b0.w};
+    *(lds_v4u*)(st_b + sob + 16) = v4u{b1.x, b1.y, b1.z, b1.w};
   };
 
-  // ---- scale indices for this wave: 2 row-blocks x 4 column-blocks
-  int64_t rb0 = (p.row0 + wm * 64) >> 5;
-  int64_t rbs[2] = {rb0 < p.sa_rows ? rb0 : p.sa_rows - 1, rb0 + 1 < p.sa_rows ? rb0 + 1 : p.sa_rows - 1};
-  int cbs[4];
+  // ---- fragment read addresses.  A: row wm*64 + i*16 + (lane&15), chunk lane>>4;
+  // the swizzle term depends only on the lane, so sub-tile i is +1024 bytes.
+  const int fr_lo = lane & 15, fr_kc = lane >> 4;
+  const lds_u8* const rd_a = sA + a_lds_off(wm * 64 + fr_lo, fr_kc);
+  // B (transposed reads): lane (g, r, c) = (lane>>4, (lane>>2)&3, lane&3) reads row
+  // k = 8g + 4h + r, 32-byte chunk J = wn*8 + j at position J ^ r, byte 8c.
+  // J ^ r = wn*8 + 4*(j>>2) + ((j&3) ^ r): four lane-dependent bases, the rest
+  // (h, j>>2, the stage) compile-time offsets.
+  const int tr_g = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
+  const lds_u8* rd_b[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int64_t cb = ((p.col0 + wn * 128) >> 5) + j;
-    cbs[j] = (int)(cb < NB ? cb : NB - 1);
-  }
-  const float* sa_r0 = p.sa + rbs[0] * KB;
-  const float* sa_r1 = p.sa + rbs[1] * KB;
+  for (int jj = 0; jj < 4; ++jj)
+    rd_b[jj] = sB + b_lds_off(8 * tr_g + tr_r, wn * 8 + jj) + tr_c * 8;
+  auto read_a = [&](int st, int i) __attribute__((always_inline)) -> v8bf {
+    typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
+    return *(lds_v8bf*)(rd_a + st * A_STAGE_BYTES + i * 1024);
+  };
+  auto read_b = [&](int st, int j) __attribute__((always_inline)) -> v8bf {
+    const lds_u8* base = rd_b[j & 3] + st * B_STAGE_BYTES + (j >> 2) * 128;
+    v4s h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base));
+    v4s h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 4 * 512));
+    v2i x0 = __builtin_bit_cast(v2i, h0), x1 = __builtin_bit_cast(v2i, h1);
+    return __builtin_bit_cast(v8bf, v4i{x0[0], x0[1], x1[0], x1[1]});
+  };
+
+  // ---- scales.  Window buffer [2][sa: 8 row-blocks x SCW][sb: 8 col-blocks x SCW]
+  // (K-block minor).  Each thread copies up to 4 values per window; rows or
+  // columns past the operand are clamped to a valid block (never stored).
+  float* const sc_lds = reinterpret_cast<float*>(smem + TILE_STAGES * STAGE_BYTES);  // after A and B stages
+  const int64_t rb_tile = p.row0 >> 5, cb_tile = p.col0 >> 5;
+  auto load_scale_window = [&](int win) __attribute__((always_inline)) {
+    float* dst = sc_lds + (win & 1) * (2 * 8 * SCW);
+#pragma unroll
+    for (int e = t; e < 2 * 8 * SCW; e += TTHREADS) {
+      const int which = e / (8 * SCW), rem = e % (8 * SCW);
+      const int blk = rem / SCW, kk = win * SCW + rem % SCW;
+      float v = 0.0f;
+      if (kk < KB) {
+        if (which == 0) {
+          int64_t rb = rb_tile + blk;
+          rb = rb < p.sa_rows ? rb : p.sa_rows - 1;
+          v = p.sa[rb * KB + kk];
+        } else {
+          int64_t cb = cb_tile + blk;
+          cb = cb < NB ? cb : NB - 1;
+          v = p.sb[(int64_t)kk * NB + cb];
+        }
+      }
+      dst[e] = v;
+    }
+  };
+  // this wave's blocks: rows wm*64.. (row-blocks 2wm, 2wm+1), cols wn*128.. (col-blocks 4wn..4wn+3)
+  // raw scales of one K-block for this wave: sa of its 2 row-blocks, sb of its 4 column-blocks
+  auto read_scales = [&](int kb, float (&sc)[6]) __attribute__((always_inline)) {
+    const float* w0 = sc_lds + ((kb / SCW) & 1) * (2 * 8 * SCW);
+    const int kk = kb % SCW;
+    sc[0] = w0[(2 * wm) * SCW + kk];
+    sc[1] = w0[(2 * wm + 1) * SCW + kk];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[2 + j] = w0[8 * SCW + (4 * wn + j) * SCW + kk];
+  };
 
   v4f acc[4][8];
 #pragma unroll
@@ -110,66 +177,77 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // fragment read offsets (relative to a stage)
-  const int fr_row_lo = lane & 15, fr_kc = lane >> 4;
-  const int tr_g = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
-
-  uint4 ra, rb;
-  if (KB > 0) {
-    load_stage(0, ra, rb);
-    store_stage(0, ra, rb);
-    if (KB > 1) load_stage(1, ra, rb);
-  }
+  // ---- prologue: K-blocks 0 and 1 staged in LDS, K-block 2 in registers,
+  // K-block 0's fragments in registers
+  load_scale_window(0);
+  uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
+  if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
+  if (KB > 1) { load_stage(1, ra, rb); store_stage(1, ra, rb); }
+  if (KB > 0) load_stage(KB > 2 ? 2 : KB - 1, ra, rb);
   __syncthreads();
+  v8bf af[4], bfrag[8];
+  if (KB > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = read_a(0, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bfrag[j] = read_b(0, j);
+  }
 
+  // Ring of three bf16 stages: in the iteration for K-block kb (stage kb%3 is
+  // already in registers), stage (kb+1)%3 (written one iteration earlier) is
+  // read for the next iteration while this one computes, and stage (kb+2)%3
+  // receives the K-block held in registers.  One barrier per iteration orders
+  // the three.
+  int sn = 1, sf = 2;  // stages (kb+1)%3 and (kb+2)%3, wave-uniform
+  float sc_cur[6];
+  read_scales(0, sc_cur);
   for (int kb = 0; kb < KB; ++kb) {
-    const int cur = kb & 1;
-    const unsigned char* sA = smem + cur * STAGE_BYTES;
-    const unsigned char* sB = sA + A_STAGE_BYTES;
-
-    // scales for this K-block
-    float s_a0 = sa_r0[kb], s_a1 = sa_r1[kb];
-    float s_b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_b[j] = p.sb[(int64_t)kb * NB + cbs[j]];
-
-    // fragments
-    v8bf af[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 64 + i * 16 + fr_row_lo;
-      af[i] = *reinterpret_cast<const v8bf*>(sA + a_lds_off(row, fr_kc));
-    }
-    v8bf bfrag[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int J = wn * 8 + j;
-      v4s h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4s_t*)(sB + b_lds_off(8 * tr_g + tr_r, J) + tr_c * 8));
-      v4s h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4s_t*)(sB + b_lds_off(8 * tr_g + 4 + tr_r, J) + tr_c * 8));
-      v2i x0 = __builtin_bit_cast(v2i, h0), x1 = __builtin_bit_cast(v2i, h1);
-      bfrag[j] = __builtin_bit_cast(v8bf, v4i{x0[0], x0[1], x1[0], x1[1]});
-    }
-
-    // stage the next K-block into the other buffer while this one is consumed
-    if (kb + 1 < KB) {
-      store_stage(cur ^ 1, ra, rb);
-      if (kb + 2 < KB) load_stage(kb + 2, ra, rb);
-    }
-
-    float s[2][4];
+    // next window of scales: written now, first read SCW iterations later
+    if (kb % SCW == 0 && kb + SCW < KB) load_scale_window(kb / SCW + 1);
+    // the scales of the next K-block, read one iteration ahead
+    float sc_nxt[6];
+    read_scales(kb + 1 < KB ? kb + 1 : kb, sc_nxt);
+    float s_cur[2][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      s[0][j] = s_a0 * s_b[j];
-      s[1][j] = s_a1 * s_b[j];
+      s_cur[0][j] = sc_cur[0] * sc_cur[2 + j];
+      s_cur[1][j] = sc_cur[1] * sc_cur[2 + j];
+    }
+
+    // 32 sub-tile partials, j outer, so that each B fragment is dead after its
+    // four uses and is refilled with the next K-block's; partials pass through
+    // a ring of PDEPTH registers so PDEPTH MFMAs are in flight while the VALU
+    // promotes the oldest.  The staging of K-block kb+2 (decode + LDS stores)
+    // goes in after the first group of MFMAs.
+    constexpr int PDEPTH = 3;
+    v4f pr[PDEPTH];
+#pragma unroll
+    for (int q = 0; q < 32 + PDEPTH; ++q) {
+      if (q >= PDEPTH) {
+        const int u = q - PDEPTH;
+        const int ui = u & 3, uj = u >> 2;
+        promote(acc[ui][uj], pr[u % PDEPTH], s_cur[ui >> 1][uj >> 1]);
+      }
+      if (q < 32) {
+        const int qi = q & 3, qj = q >> 2;
+        pr[q % PDEPTH] = mfma_partial(af[qi], bfrag[qj]);
+        if (qi == 3) bfrag[qj] = read_b(sn, qj);  // last use of this B fragment
+        if (qj == 7) af[qi] = read_a(sn, qi);     // last use of this A fragment
+      }
+      if (q == 4) {
+        // Unconditional (clamped) staging: a branch here would keep the old and
+        // new register contents alive together.  Past the end the stage written
+        // is never read.
+        store_stage(sf, ra, rb);
+        load_stage(kb + 3 < KB ? kb + 3 : KB - 1, ra, rb);
+      }
+      if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) promote(acc[i][j], mfma_partial(af[i], bfrag[j]), s[i >> 1][j >> 1]);
-
+    for (int i = 0; i < 6; ++i) sc_cur[i] = sc_nxt[i];
     __syncthreads();
+    sn = sn == 2 ? 0 : sn + 1;
+    sf = sf == 2 ? 0 : sf + 1;
   }
 
   // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
