@@ -8,7 +8,7 @@ measured step time (TFLOP/s of the whole path).
 
 Also measured (same run, reported under "detail"):
   * the GEMM kernel alone, per launch with HIP events on the launch stream, with
-    the caches flushed before each launch (a 1 GiB fill), and its roofline
+    the caches flushed before each launch (a 1 GiB read), and its roofline
     against MI355X's dense FP8 MFMA peak;
   * the small-M (decode) GEMM at K=8192, M in {1, 8, 32, 64}, N in
     {8192, 28672}: algorithmic HBM bytes per launch over the kernel time;
@@ -72,10 +72,15 @@ def main():
     def to_dev_bf16(bits):
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Cache flush between timed launches: READ 1 GiB (written once, here).  A
+    # read evicts L2 and the 256 MB Infinity Cache and leaves only clean lines;
+    # a write flush would leave dirty lines whose write-back then runs inside
+    # the next timed launch and halves the bandwidth it sees.
+    flush_buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
 
     def flush():
-        flush_buf.fill_(1)  # 1 GiB of writes evicts L2 and the 256 MB Infinity Cache
+        flush_buf.sum()
 
     def time_launch(fn, reps, do_flush=True):
         """Median and min per-launch time in ms, HIP events on the launch stream."""

@@ -26,6 +26,8 @@
 //    K-block order - the same sequence of roundings as the tile kernel.
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace fp8bs {
 
 // ------------------------------------------------------------------------------------
@@ -384,110 +386,208 @@ __global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* _
 // ------------------------------------------------------------------------------------
 // small-M kernel
 // ------------------------------------------------------------------------------------
-constexpr int SBN = 32;          // columns per workgroup
-constexpr int SWAVES = 8;        // K-blocks formed per round (one per wave)
+constexpr int SWAVES = 8;        // waves per workgroup; also K-blocks per round
 constexpr int STHREADS = SWAVES * 64;
+constexpr int SMALL_LDS_BUDGET = 160 * 1024;
 
-// Per-wave B staging (E4M3, 32 k x 32 bytes) with the two 16-byte halves of
-// row k swapped when bit 2 of k is set, which makes the transposed reads free
-// of bank conflicts.
-__device__ __forceinline__ int sb_lds_off(int k, int half) { return k * 32 + ((half ^ ((k >> 2) & 1)) << 4); }
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4:
+// lane l's bytes land at M0 + 16*l; M0 = LDS byte address of the wave's 1 KB
+// destination).  Issued from inline asm so that the compiler does not drain
+// every load before the next LDS read; the callers wait with explicit vmcnt
+// counts (a wave's loads complete in issue order).  Nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
+               : "memory");
+}
+// The same with 4 bytes per lane (lane l's dword lands at M0 + 4*l).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr)
+               : "memory");
+}
+// Workgroup barrier that orders LDS only: the direct loads in flight keep
+// running (a plain __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-template <int MT>  // number of 16-row MFMA sub-tiles (M <= 16 * MT)
+// Small-M kernel: a workgroup owns W = 32*NCB columns of C for all M <= 64
+// rows and all of K.  K-blocks are streamed in rounds of eight: in round r,
+// wave q loads K-block 8r+q (B tile 32 x W bytes, the A rows, the scales) into
+// its own slot of an LDS ring D rounds deep.  After one barrier every wave
+// reads all eight slots and runs the promotion chain of the 16x16 output
+// sub-tiles it owns, K-block by K-block in ascending order, so no partial
+// result ever crosses waves.
+//
+// B tile layout in a slot: row k (32 rows of W bytes), 16-byte piece p holds
+// global piece p ^ f(k), where f(k) = (k / (256/W)) mod (2*NCB): the sixteen
+// rows that one 32-lane phase of a transposed read touches land in sixteen
+// different 16-byte bank groups.
+template <int MT, int NCB>
+struct SmallMCfg {
+  static constexpr int W = 32 * NCB;                   // columns (= bytes of a B row) per workgroup
+  static constexpr int ACH = (MT + 1) / 2;             // 1 KB chunks of A rows (32 rows each)
+  static constexpr int B_BYTES = 32 * W;
+  static constexpr int SC_OFF = B_BYTES + ACH * 1024;  // 256-byte scale record after B and A
+  static constexpr int SLOT = SC_OFF + 256;
+  static constexpr int D_FIT = SMALL_LDS_BUDGET / (SWAVES * SLOT);
+  static constexpr int D = D_FIT > 6 ? 6 : D_FIT;      // ring depth in rounds
+  static constexpr int LDS = SWAVES * D * SLOT;
+  static constexpr int OPS = NCB + ACH + 1;            // direct loads per K-block
+  static constexpr int CS = 2 * NCB;                   // 16-column sub-tiles per workgroup
+  static constexpr int RG = SWAVES / CS;               // row-tile groups
+  static constexpr int TPW = (MT + RG - 1) / RG;       // row tiles per wave (at most)
+  static_assert(D >= 3, "ring too shallow");
+  static_assert(LDS <= SMALL_LDS_BUDGET, "LDS budget");
+  static_assert((D - 2) * OPS < 64, "vmcnt range");
+};
+
+template <int NCB>
+__device__ __forceinline__ int small_b_swz(int k) {
+  return (k / (8 / NCB)) & (2 * NCB - 1);
+}
+
+template <int MT, int NCB>
 __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __restrict__ a,
                                                                const float* __restrict__ sa,
                                                                const uint8_t* __restrict__ b,
                                                                const float* __restrict__ sb,
                                                                uint16_t* __restrict__ c, int64_t M, int64_t N,
                                                                int64_t K) {
-  // LDS: B staging [8 waves][1 KB], partials [8 waves][MT][2][64 lanes] v4f
-  __shared__ __attribute__((aligned(16))) unsigned char s_b[SWAVES][1024];
-  __shared__ v4f s_p[SWAVES][MT * 2 * 64];
+  using Cfg = SmallMCfg<MT, NCB>;
+  constexpr int D = Cfg::D, W = Cfg::W;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int t = threadIdx.x, lane = t & 63;
+  const int lane = threadIdx.x & 63;
   const int w = wave_id_uniform();
   const int KB = (int)(K >> 5), NB = (int)(N >> 5);
-  // XCD-aware: workgroups on one XCD take adjacent column slices so the 128-byte
-  // lines of B they share are fetched into that XCD's L2 once.
-  const int64_t n_slices = N / SBN;
+  // Workgroups on one XCD (blockIdx mod 8) take adjacent column slices, so the
+  // 128-byte lines of B that narrow slices share are fetched into that XCD's L2 once.
+  const int64_t n_slices = N / W;
   const int64_t id = blockIdx.x;
   const int64_t slice = (n_slices & 7) ? id : (id & 7) * (n_slices >> 3) + (id >> 3);
-  const int64_t n0 = slice * SBN;
-  const int cb = (int)(n0 >> 5);
+  const int64_t n0 = slice * W;
+  const int cb0 = (int)(n0 >> 5);
 
-  // this wave's B load: row (lane >> 1), 16-byte half (lane & 1)
-  const int bl_k = lane >> 1, bl_h = lane & 1;
-  const uint8_t* b_src = b + (int64_t)bl_k * N + n0 + bl_h * 16;
-  // A fragment rows for this lane
-  const int a_kc = lane >> 4;
-
-  // chain ownership: thread t promotes (i, j, lane) = decode(t) when t < MT*2*64
-  const int ch_i = t / 128, ch_j = (t >> 6) & 1, ch_l = t & 63;
-  const bool ch_active = t < MT * 2 * 64;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int rounds = (KB + SWAVES - 1) / SWAVES;
-  uint4 rb_next = make_uint4(0, 0, 0, 0);
-  v2i ra_next[MT];
-  auto load = [&](int kb, uint4& rbv, v2i* rav) {
-    if (kb < KB) {
-      rbv = *reinterpret_cast<const uint4*>(b_src + (int64_t)kb * 32 * N);
+  // ---- this wave's direct loads for one K-block ----
+  // B: instruction i covers rows i*(32/NCB) ... ; lane l -> row k, LDS piece p.
+  constexpr int LPR = W / 16;  // lanes per B row
+  const uint8_t* b_src[NCB];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int64_t row = i * 16 + (lane & 15);
-        rav[i] = row < M ? *reinterpret_cast<const v2i*>(a + row * K + (int64_t)kb * 32 + a_kc * 8) : v2i{0, 0};
+  for (int i = 0; i < NCB; ++i) {
+    const int k = i * (64 / LPR) + lane / LPR, p = lane % LPR;
+    b_src[i] = b + (int64_t)k * N + n0 + 16 * (p ^ small_b_swz<NCB>(k));
+  }
+  // A: chunk ch covers rows 32ch..32ch+31; lane l loads row 32ch + (l>>1),
+  // 16-byte half l&1.  Rows past M read row M-1: their results are never stored.
+  const uint8_t* a_src[Cfg::ACH];
+#pragma unroll
+  for (int ch = 0; ch < Cfg::ACH; ++ch) {
+    int64_t row = ch * 32 + (lane >> 1);
+    row = row < M ? row : M - 1;
+    a_src[ch] = a + row * K + (lane & 1) * 16;
+  }
+  // Scales: lanes 0, 1 load sa of row-blocks 0, 1 (clamped to the last one);
+  // lanes 2 .. 2+NCB-1 load sb of the workgroup's column blocks (the rest repeat the last).
+  const int nrb = (int)((M + 31) >> 5);
+  const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
+  const float* const sc_src = lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sb + cb0 + sbj;
+  const int64_t sc_stride = lane < 2 ? 1 : NB;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t ring_w = (uint32_t)(uintptr_t)((lds_u8*)(smem + w * D * Cfg::SLOT));
+
+  auto issue = [&](int r) __attribute__((always_inline)) {
+    const int kb = r * SWAVES + w;
+    const int kc = kb < KB ? kb : KB - 1;  // past the end: reload the last block (an L2 hit)
+    const uint32_t sl = ring_w + (r % D) * Cfg::SLOT;
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) dma16(b_src[i] + (int64_t)kc * 32 * N, sl + i * 1024);
+#pragma unroll
+    for (int ch = 0; ch < Cfg::ACH; ++ch) dma16(a_src[ch] + (int64_t)kc * 32, sl + Cfg::B_BYTES + ch * 1024);
+    dma4(sc_src + kc * sc_stride, sl + Cfg::SC_OFF);
+  };
+
+  // ---- ownership: 16-column sub-tile cs, row tiles rg, rg + RG, ... ----
+  const int cs = w % Cfg::CS;
+  const int rg = Cfg::RG == 1 ? 0 : w / Cfg::CS;
+  const int own_cb = cs >> 1;  // column block (within the slice) of the sub-tile
+  const bool owns = rg < MT;   // wave-uniform: waves past the last row tile only load
+  // row tile of slot t; a wave's slots past the last row tile repeat it (never stored)
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
+    const int i = rg + t * Cfg::RG;
+    return i < MT ? i : MT - 1;
+  };
+  v4f acc[Cfg::TPW];
+#pragma unroll
+  for (int t = 0; t < Cfg::TPW; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // transposed-read address of this lane's B fragment inside a slot
+  const int L = lane & 15;
+  const int bk = 8 * (lane >> 4) + (L >> 1);
+  const int b_frag_off = bk * W + 16 * (cs ^ small_b_swz<NCB>(bk)) + 8 * (L & 1);
+  const int a_frag_off = Cfg::B_BYTES + (lane & 15) * 32 + (lane >> 4) * 8;
+
+  // One round: all LDS reads first, then per K-block q (ascending) the MFMA
+  // partials of the owned tiles and their promotion.  FULL: all eight K-blocks
+  // exist (every round but possibly the last).
+  auto compute = [&](int slot, int nkb, auto FULL_) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(FULL_)::value;
+    v2i braw[SWAVES];
+    v2i araw[SWAVES][Cfg::TPW];
+    float sbv[SWAVES], sav[SWAVES][2];
+#pragma unroll
+    for (int q = 0; q < SWAVES; ++q) {
+      const unsigned char* sl = smem + (q * D + slot) * Cfg::SLOT;
+      braw[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(sl + b_frag_off));
+#pragma unroll
+      for (int t = 0; t < Cfg::TPW; ++t)
+        araw[q][t] = *reinterpret_cast<const v2i*>(sl + a_frag_off + tile_of(t) * 16 * 32);
+      const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF);
+      sav[q][0] = scr[0];
+      sav[q][1] = scr[1];
+      sbv[q] = scr[2 + own_cb];
+    }
+#pragma unroll
+    for (int q = 0; q < SWAVES; ++q) {
+      const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
+#pragma unroll
+      for (int t = 0; t < Cfg::TPW; ++t) {
+        const v4f p = mfma_partial(e4m3x8_to_bf16x8(araw[q][t]), bfrag);
+        const float sc = sav[q][tile_of(t) >> 1] * sbv[q];
+        if (FULL || q < nkb) promote(acc[t], p, sc);
       }
     }
   };
-  load(w, rb_next, ra_next);
+
+  const int rounds = (KB + SWAVES - 1) / SWAVES;
+  const int full_rounds = KB / SWAVES;
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d) issue(d);
 
   for (int r = 0; r < rounds; ++r) {
-    const int kb = r * SWAVES + w;
-    uint4 rbv = rb_next;
-    v2i rav[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) rav[i] = ra_next[i];
-    load(kb + SWAVES, rb_next, ra_next);  // prefetch the next round
-
-    if (kb < KB) {
-      // B tile -> LDS (wave-private), then transposed 8-byte reads
-      *reinterpret_cast<uint4*>(&s_b[w][sb_lds_off(bl_k, bl_h)]) = rbv;
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_wave_barrier();
-      v8bf bfrag[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int L = lane & 15;
-        const int k = 8 * (lane >> 4) + (L >> 1);
-        v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)&s_b[w][sb_lds_off(k, j) + 8 * (L & 1)]);
-        bfrag[j] = e4m3x8_to_bf16x8(x);
-      }
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        v8bf af = e4m3x8_to_bf16x8(rav[i]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) s_p[w][(i * 2 + j) * 64 + lane] = mfma_partial(af, bfrag[j]);
-      }
+    wait_vmcnt<(D - 2) * Cfg::OPS>();  // this wave's round-r loads have landed
+    lds_barrier();                     // ... and everyone else's; round r-1's slots are free
+    issue(r + D - 1);                  // refill the slot that round r-1 used
+    if (owns) {
+      if (r < full_rounds) compute(r % D, SWAVES, std::true_type{});
+      else compute(r % D, KB - r * SWAVES, std::false_type{});
     }
-    __syncthreads();
-    if (ch_active) {
-      const int nkb = (KB - r * SWAVES) < SWAVES ? (KB - r * SWAVES) : SWAVES;
-      const int64_t rbk = (ch_i * 16) >> 5;  // row-block of this sub-tile
-      for (int q = 0; q < nkb; ++q) {
-        const int kbq = r * SWAVES + q;
-        const float s = sa[rbk * KB + kbq] * sb[(int64_t)kbq * NB + cb];
-        promote(acc, s_p[q][(ch_i * 2 + ch_j) * 64 + ch_l], s);
-      }
-    }
-    __syncthreads();
   }
+  wait_vmcnt<0>();  // drain the extra loads before the workgroup ends
 
-  if (ch_active) {
-    const int col = (int)n0 + ch_j * 16 + (ch_l & 15);
+  const int col = (int)n0 + cs * 16 + (lane & 15);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int64_t row = ch_i * 16 + 4 * (ch_l >> 4) + rr;
-      if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[rr]);
+  for (int t = 0; t < Cfg::TPW; ++t) {
+    const int i = rg + t * Cfg::RG;
+    if (owns && i < MT) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
+        if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+      }
     }
   }
 }
@@ -516,37 +616,71 @@ hipError_t launch_gemm_grouped(const void* a, const float* sa, const void* b, co
   return hipGetLastError();
 }
 
+// Column-slice width for the small-M kernel: 128-byte slices read whole cache
+// lines of B, but the grid must still cover most of the 256 CUs.
+int smallm_ncb(int64_t N) {
+  if (N % 128 == 0 && N / 128 >= 192) return 4;
+  if (N % 64 == 0 && N / 64 >= 192) return 2;
+  return 1;
+}
+
+template <int MT, int NCB>
+static void launch_smallm_t(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  using Cfg = SmallMCfg<MT, NCB>;
+  hipLaunchKernelGGL((gemm_smallm_kernel<MT, NCB>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS, stream,
+                     a, sa, b, sb, c, M, N, K);
+}
+
+template <int NCB>
+static void launch_smallm_n(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  switch ((int)((M + 15) / 16)) {
+    case 1: launch_smallm_t<1, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 2: launch_smallm_t<2, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 3: launch_smallm_t<3, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
+    default: launch_smallm_t<4, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
+  }
+}
+
 hipError_t launch_gemm_smallm(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
                               int64_t N, int64_t K, hipStream_t stream) {
-  const int64_t grid = N / SBN;
-  const int mt = (int)((M + 15) / 16);
-  switch (mt) {
-    case 1:
-      hipLaunchKernelGGL(gemm_smallm_kernel<1>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
-                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
-      break;
-    case 2:
-      hipLaunchKernelGGL(gemm_smallm_kernel<2>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
-                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
-      break;
-    case 3:
-      hipLaunchKernelGGL(gemm_smallm_kernel<3>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
-                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
-      break;
-    default:
-      hipLaunchKernelGGL(gemm_smallm_kernel<4>, dim3((unsigned)grid), dim3(STHREADS), 0, stream, (const uint8_t*)a,
-                         sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K);
-      break;
+  const uint8_t* a8 = (const uint8_t*)a;
+  const uint8_t* b8 = (const uint8_t*)b;
+  uint16_t* c16 = (uint16_t*)c;
+  switch (smallm_ncb(N)) {
+    case 4: launch_smallm_n<4>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+    case 2: launch_smallm_n<2>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+    default: launch_smallm_n<1>(a8, sa, b8, sb, c16, M, N, K, stream); break;
   }
   return hipGetLastError();
+}
+
+template <int MT, int NCB>
+static hipError_t set_smallm_attr() {
+  return hipFuncSetAttribute((const void*)gemm_smallm_kernel<MT, NCB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             SmallMCfg<MT, NCB>::LDS);
+}
+
+template <int NCB>
+static hipError_t set_smallm_attrs() {
+  hipError_t e;
+  if ((e = set_smallm_attr<1, NCB>()) != hipSuccess) return e;
+  if ((e = set_smallm_attr<2, NCB>()) != hipSuccess) return e;
+  if ((e = set_smallm_attr<3, NCB>()) != hipSuccess) return e;
+  return set_smallm_attr<4, NCB>();
 }
 
 hipError_t set_gemm_attributes() {
   hipError_t e = hipFuncSetAttribute((const void*)gemm_tile_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      TILE_LDS_BYTES);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             TILE_LDS_BYTES);
+  e = hipFuncSetAttribute((const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          TILE_LDS_BYTES);
+  if (e != hipSuccess) return e;
+  if ((e = set_smallm_attrs<1>()) != hipSuccess) return e;
+  if ((e = set_smallm_attrs<2>()) != hipSuccess) return e;
+  return set_smallm_attrs<4>();
 }
 
 }  // namespace fp8bs

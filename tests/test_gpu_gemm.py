@@ -37,6 +37,8 @@ def _assert_tol(c_bits, ref, absref, label):
     (520, 288, 160),      # three M-tiles, two N-tiles, ragged tails
     (1, 64, 256), (8, 96, 128), (33, 32, 64), (64, 160, 96),   # small-M kernel
     (65, 64, 64),         # just above the small-M limit
+    (1, 24576, 96), (40, 24576, 64),      # small-M kernel, 128-column slices
+    (64, 12288, 96), (17, 12288, 320),    # small-M kernel, 64-column slices; ragged last round
 ])
 def test_gemm_matches_oracle(M, N, K):
     qa, sa = _quantized(2000 + M, M, K)
@@ -128,6 +130,26 @@ def test_rows_independent_of_batch():
         say(f"invariance prefix M={m}")
         pre = gpu_gemm(qa[:m], sa[:-(-m // 32)], qb, sb)
         assert np.array_equal(pre, full[:m])
+
+
+@pytest.mark.parametrize("N", [12288, 24576])
+def test_rows_independent_of_batch_wide_slices(N):
+    """The small-M kernel's 64- and 128-column slice variants give the tile
+    kernel's bits, row by row."""
+    qa, sa = _quantized(29, 320, 160)
+    qb, sb = _quantized(30, 160, N, std=0.02)
+    say(f"wide invariance full M=320 N={N}")
+    full = gpu_gemm(qa, sa, qb, sb)
+    ref, absref = oracle.gemm_ref(qa, sa, qb, sb)
+    _assert_tol(full, ref, absref, f"wide M=320 N={N}")
+    for m in (64, 33, 8, 1):
+        say(f"wide invariance prefix M={m} N={N}")
+        pre = gpu_gemm(qa[:m], sa[:-(-m // 32)], qb, sb)
+        assert np.array_equal(pre, full[:m]), f"M={m}"
+    for i in (7, 200):
+        say(f"wide invariance row {i} N={N}")
+        one = gpu_gemm(qa[i:i + 1], sa[i // 32:i // 32 + 1], qb, sb)
+        assert np.array_equal(one[0], full[i]), f"row {i}"
 
 
 def test_row_blocks_permute_and_repeat():
