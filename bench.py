@@ -80,7 +80,7 @@ def main():
     torch.cuda.synchronize()
 
     def flush():
-        flush_buf.sum()
+        flush_buf.max()  # a read-only reduction (sum would first widen to an int64 copy)
 
     def time_launch(fn, reps, do_flush=True):
         """Median and min per-launch time in ms, HIP events on the launch stream."""
@@ -121,14 +121,17 @@ def main():
         for _ in range(3):
             step()
         torch.cuda.synchronize()
-        # one decode shape so its kernel shows up too
-        dwl = W.decode(8, 8192)
-        da = to_dev_bf16(dwl.a_bits())
-        db = to_dev_bf16(dwl.b_bits())
-        dqa, dsa = fp8bs.quantize(da)
-        dqb, dsb = fp8bs.quantize(db)
-        for _ in range(3):
-            fp8bs.gemm(dqa, dsa, dqb, dsb)
+        # decode M=8 at both widths so both small-M kernel variants show up
+        for n_dec in (8192, 28672):
+            dwl = W.decode(8, n_dec)
+            da = to_dev_bf16(dwl.a_bits())
+            db = to_dev_bf16(dwl.b_bits())
+            dqa, dsa = fp8bs.quantize(da)
+            dqb, dsb = fp8bs.quantize(db)
+            for _ in range(3):
+                flush()
+                fp8bs.gemm(dqa, dsa, dqb, dsb)
+            del da, db, dqa, dsa, dqb, dsb
         # plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
         dst = torch.empty_like(src)
