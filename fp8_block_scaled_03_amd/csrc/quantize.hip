@@ -8,80 +8,125 @@
 // (round to nearest even, E4M3FN) after clamping to +-448 (the converter would
 // produce NaN above 464); an all-zero block gets s = 0 and 0x00 codes.
 //
-// Mapping: one wave per 32x32 block.  Lane l owns row l/2 of the block and 16
-// consecutive columns (32 bytes of bf16 in, 16 bytes of codes out); the block
-// amax is a 64-lane max reduction.  The kernel is bound by HBM traffic
-// (2 bytes read + 1 byte written per element) and by the fp32 divide.
+// The quotient.  x / s (IEEE, round to nearest even) costs about ten VALU
+// instructions; instead each block forms r = RN(1/s) with one IEEE division and
+// every element takes q0 = RN(x*r), e = x - s*q0 (exact, one fma), t =
+// RN(q0 + e*r) (one fma).  With r the correctly rounded reciprocal and q0
+// within an ulp of x/s this final correction returns RN(x/s) (Markstein's
+// theorem, P. Markstein, IBM J. Res. Dev. 34(1), 1990), provided the remainder
+// e does not underflow: that holds for |x| >= 2^-102, and blocks with
+// amax >= 2^-60 send every smaller |x| to |x/s| < 2^-33, which becomes a zero
+// code whatever its last bits.  Blocks with a smaller amax, where s is tiny,
+// divide directly.  The sign is copied from x so that -0 stays -0.
+//
+// The kernel is bound by HBM traffic (2 bytes read + 1 byte written per
+// element); the mapping below keeps 128 bytes per lane in flight.
 #include "common.hpp"
+
+#include <type_traits>
 
 namespace fp8bs {
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Max over the 16 lanes that hold one block (lane bits 0, 1, 4, 5).
+__device__ __forceinline__ float block_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1, 64));
+  v = fmaxf(v, __shfl_xor(v, 2, 64));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
   return v;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
+constexpr int Q_BLOCKS = 4;  // 32x32 blocks per wave region (32 rows x 128 columns)
+
+// One wave per region of 32 rows x 128 columns (256 bytes of bf16 per row).
+// Load k (0..7) of lane l reads 16 bytes: row 4k + (l>>4), byte 16*(l&15) of
+// the region row, so one load instruction covers four whole region rows.  A
+// lane therefore holds 8 rows x 8 columns of block b = (l>>2)&3, and a block's
+// amax is a max over its 16 lanes.  All eight loads are in flight before any
+// arithmetic.  Regions past the last column block hold fewer blocks; the
+// missing ones load nothing and store nothing.
 __global__ void __launch_bounds__(256) quantize_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                        uint8_t* __restrict__ q, float* __restrict__ scales,
-                                                       int64_t n_blocks) {
+                                                       int64_t n_regions) {
   const int lane = threadIdx.x & 63;
+  const int piece = lane & 15, rsub = lane >> 4;
+  const int b = piece >> 2, cpart = piece & 3;
   const int64_t cb_count = cols >> 5;
+  const int64_t rg_per_row = (cb_count + Q_BLOCKS - 1) / Q_BLOCKS;
   const int64_t waves_total = (int64_t)gridDim.x * 4;
-  for (int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); blk < n_blocks; blk += waves_total) {
-    const int64_t rb = blk / cb_count, cb = blk - rb * cb_count;
-    const int64_t row = rb * 32 + (lane >> 1);
-    const int64_t col = cb * 32 + (lane & 1) * 16;
-    const bool valid = row < rows;
-    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
-    if (valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + row * cols + col);
-      w0 = src[0];
-      w1 = src[1];
-    }
-    float v[16];
-    const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  for (int64_t reg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); reg < n_regions; reg += waves_total) {
+    const int64_t rb = reg / rg_per_row, g = reg - rb * rg_per_row;
+    const int64_t cb = g * Q_BLOCKS + b;
+    const bool cb_ok = cb < cb_count;
+    const int64_t col = (cb_ok ? cb : cb_count - 1) * 32 + cpart * 8;  // stays inside x
+    uint4 w[8];
+    bool ok[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = bf16_lo(ws[i]);
-      v[2 * i + 1] = bf16_hi(ws[i]);
+    for (int k = 0; k < 8; ++k) {
+      const int64_t row = rb * 32 + 4 * k + rsub;
+      ok[k] = cb_ok && row < rows;
+      const int64_t rc = row < rows ? row : rows - 1;
+      w[k] = ok[k] ? *reinterpret_cast<const uint4*>(x + rc * cols + col) : make_uint4(0, 0, 0, 0);
     }
+    // values are re-derived from the loaded words where needed, so only the
+    // 32 dwords of raw bf16 stay live
     float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-    const float amax = wave_max(m);
-    const float s = amax / 448.0f;
-    uint32_t packed[4];
-    if (s != 0.0f) {
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t0 = fminf(fmaxf(v[4 * i + 0] / s, -448.0f), 448.0f);
-        float t1 = fminf(fmaxf(v[4 * i + 1] / s, -448.0f), 448.0f);
-        float t2 = fminf(fmaxf(v[4 * i + 2] / s, -448.0f), 448.0f);
-        float t3 = fminf(fmaxf(v[4 * i + 3] / s, -448.0f), 448.0f);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, w, true);
-        packed[i] = (uint32_t)w;
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[i])), fabsf(bf16_hi(ws[i]))));
+    }
+    const float amax = block_max(m);
+    const float s = amax / 448.0f;
+    const bool recip = amax >= 0x1p-60f;  // wave-uniform per block
+    const float r = recip ? 1.0f / s : 0.0f;
+    auto quotient = [&](float xv, auto FAST_) __attribute__((always_inline)) -> float {
+      if (decltype(FAST_)::value || recip) {
+        const float q0 = xv * r;
+        const float e = __builtin_fmaf(-q0, s, xv);
+        return __builtin_copysignf(__builtin_fmaf(e, r, q0), xv);
       }
-    } else {
-      packed[0] = packed[1] = packed[2] = packed[3] = 0u;
-    }
-    if (valid) {
-      *reinterpret_cast<uint4*>(q + row * cols + col) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    }
-    if (lane == 0) scales[rb * cb_count + cb] = s;
+      return s != 0.0f ? xv / s : 0.0f;
+    };
+    auto encode_store = [&](auto FAST_) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        uint32_t packed[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float t0 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i]), FAST_), -448.0f), 448.0f);
+          const float t1 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i]), FAST_), -448.0f), 448.0f);
+          const float t2 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i + 1]), FAST_), -448.0f), 448.0f);
+          const float t3 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i + 1]), FAST_), -448.0f), 448.0f);
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, wd, true);
+          packed[i] = (uint32_t)wd;
+        }
+        if (ok[k]) {
+          const int64_t row = rb * 32 + 4 * k + rsub;
+          *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
+        }
+      }
+    };
+    // every block of the wave on the reciprocal path (the common case): no
+    // per-element branches
+    if (__all(recip)) encode_store(std::true_type{});
+    else encode_store(std::false_type{});
+    if (cpart == 0 && rsub == 0 && cb_ok) scales[rb * cb_count + cb] = s;
   }
 }
 
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, void* q, float* scales, hipStream_t stream) {
-  const int64_t n_blocks = ((rows + 31) / 32) * (cols / 32);
-  int64_t grid = (n_blocks + 3) / 4;
+  const int64_t n_regions = ((rows + 31) / 32) * ((cols / 32 + Q_BLOCKS - 1) / Q_BLOCKS);
+  int64_t grid = (n_regions + 3) / 4;
   if (grid > 65536) grid = 65536;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)x, rows, cols,
-                     (uint8_t*)q, scales, n_blocks);
+                     (uint8_t*)q, scales, n_regions);
   return hipGetLastError();
 }
 

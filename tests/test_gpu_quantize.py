@@ -68,6 +68,35 @@ def test_many_scales_all_bf16():
         _check(blocks.reshape(nblk, 32, 32).transpose(1, 0, 2).reshape(32, nblk * 32), f"amax={float(af):.3e}")
 
 
+def _all_bf16_under(ab):
+    """Blocks holding every finite bf16 value |x| <= amax (bits ab), each block
+    led by the amax element itself."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    xf = (bits << 16).view(np.float32)
+    allb = bits[np.isfinite(xf)].astype(np.uint16)
+    af = np.array([np.uint32(ab) << np.uint32(16)], dtype=np.uint32).view(np.float32)[0]
+    keep = allb[np.abs((allb.astype(np.uint32) << 16).view(np.float32)) <= af]
+    per = 1023
+    nblk = -(-len(keep) // per)
+    pad = np.zeros(nblk * per, np.uint16)
+    pad[:len(keep)] = keep
+    blocks = np.concatenate([np.full((nblk, 1), ab, np.uint16), pad.reshape(nblk, per)], axis=1)
+    return blocks.reshape(nblk, 32, 32).transpose(1, 0, 2).reshape(32, nblk * 32)
+
+
+@pytest.mark.parametrize("amax_bits", [
+    0x2200, 0x21FF, 0x2180, 0x2100, 0x20FF,     # around 2^-60, where the quotient method switches
+    0x0001, 0x0040, 0x0080, 0x00FF, 0x1000,     # subnormal and tiny block maxima
+    0x43E0, 0x3F80, 0x4060, 0x7F60, 0x7F7F,     # 448, 1, 3.5, 448 * 2^120, the largest bf16
+    0x3DE0, 0x48E0, 0x3F81, 0x3FFF, 0x4001,     # 448 * 2^-k, 448 * 2^k, near-power-of-two maxima
+])
+def test_targeted_scales_all_bf16(amax_bits):
+    """Every finite bf16 value under block maxima chosen at the edges of the
+    quotient computation: exact powers of two times 448 (s a power of two),
+    maxima around the switch to direct division, subnormal and huge maxima."""
+    _check(_all_bf16_under(np.uint16(amax_bits)), f"amax bits {amax_bits:#06x}")
+
+
 def test_golden_examples_on_gpu():
     x = np.full((32, 32), 0x3F80, dtype=np.uint16)
     x[0, 0] = 0x3FA3
