@@ -38,11 +38,11 @@ constexpr int A_STAGE_BYTES = TBM * 32 * 2;  // 16 KB bf16
 constexpr int B_STAGE_BYTES = 32 * TBN * 2 + 512;  // 16 KB bf16 + row-group shifts
 constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
 constexpr int TILE_STAGES = 3;
-// Scales are staged in LDS in windows of SCW K-blocks (double-buffered): per
-// window 8 row-blocks of sa and 8 column-blocks of sb.
-constexpr int SCW = 128;
-constexpr int SC_WINDOW_BYTES = 2 * 8 * SCW * 4;  // 8 KB
-constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + 2 * SC_WINDOW_BYTES;  // 112 KB
+// Scale products s = sa * sb are formed once per workgroup in windows of SCW
+// K-blocks (double-buffered in LDS): per K-block 8 row-blocks x 8 column-blocks.
+constexpr int SCW = 64;
+constexpr int SC_WINDOW_BYTES = SCW * 8 * 8 * 4;  // 16 KB
+constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + 2 * SC_WINDOW_BYTES;  // 130 KB
 
 // A tile in LDS: [256 rows][4 chunks of 8 bf16]; chunk c of row r lives at
 // position c ^ ((r >> 1) & 3).
@@ -136,41 +136,44 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     return __builtin_bit_cast(v8bf, v4i{x0[0], x0[1], x1[0], x1[1]});
   };
 
-  // ---- scales.  Window buffer [2][sa: 8 row-blocks x SCW][sb: 8 col-blocks x SCW]
-  // (K-block minor).  Each thread copies up to 4 values per window; rows or
-  // columns past the operand are clamped to a valid block (never stored).
+  // ---- scale products.  Window buffer [2][SCW K-blocks][8 row-blocks][8 col-blocks]
+  // of s = sa * sb (one fp32 multiply, the same rounding every kernel uses).
+  // Thread t forms (row-block, col-block) = ((t>>3)&7, t&7) for K-blocks
+  // t>>6, t>>6 + 8, ...; rows or columns past the operand are clamped to a
+  // valid block (never stored).
   float* const sc_lds = reinterpret_cast<float*>(smem + TILE_STAGES * STAGE_BYTES);  // after A and B stages
   const int64_t rb_tile = p.row0 >> 5, cb_tile = p.col0 >> 5;
+  const int w_rb = (t >> 3) & 7, w_cb = t & 7, w_k0 = t >> 6;
+  int64_t sa_row = rb_tile + w_rb;
+  sa_row = sa_row < p.sa_rows ? sa_row : p.sa_rows - 1;
+  int64_t sb_col = cb_tile + w_cb;
+  sb_col = sb_col < NB ? sb_col : NB - 1;
+  const float* const sa_src = p.sa + sa_row * KB;
+  const float* const sb_src = p.sb + sb_col;
   auto load_scale_window = [&](int win) __attribute__((always_inline)) {
-    float* dst = sc_lds + (win & 1) * (2 * 8 * SCW);
+    float* dst = sc_lds + (win & 1) * (SCW * 64);
+    float va[SCW / 8], vb[SCW / 8];
 #pragma unroll
-    for (int e = t; e < 2 * 8 * SCW; e += TTHREADS) {
-      const int which = e / (8 * SCW), rem = e % (8 * SCW);
-      const int blk = rem / SCW, kk = win * SCW + rem % SCW;
-      float v = 0.0f;
-      if (kk < KB) {
-        if (which == 0) {
-          int64_t rb = rb_tile + blk;
-          rb = rb < p.sa_rows ? rb : p.sa_rows - 1;
-          v = p.sa[rb * KB + kk];
-        } else {
-          int64_t cb = cb_tile + blk;
-          cb = cb < NB ? cb : NB - 1;
-          v = p.sb[(int64_t)kk * NB + cb];
-        }
-      }
-      dst[e] = v;
+    for (int i = 0; i < SCW / 8; ++i) {
+      int kk = win * SCW + w_k0 + 8 * i;
+      kk = kk < KB ? kk : KB - 1;  // past the end: any valid block (never read)
+      va[i] = sa_src[kk];
+      vb[i] = sb_src[(int64_t)kk * NB];
     }
+#pragma unroll
+    for (int i = 0; i < SCW / 8; ++i) dst[(w_k0 + 8 * i) * 64 + w_rb * 8 + w_cb] = va[i] * vb[i];
   };
   // this wave's blocks: rows wm*64.. (row-blocks 2wm, 2wm+1), cols wn*128.. (col-blocks 4wn..4wn+3)
-  // raw scales of one K-block for this wave: sa of its 2 row-blocks, sb of its 4 column-blocks
-  auto read_scales = [&](int kb, float (&sc)[6]) __attribute__((always_inline)) {
-    const float* w0 = sc_lds + ((kb / SCW) & 1) * (2 * 8 * SCW);
-    const int kk = kb % SCW;
-    sc[0] = w0[(2 * wm) * SCW + kk];
-    sc[1] = w0[(2 * wm + 1) * SCW + kk];
+  typedef float v4f_t __attribute__((ext_vector_type(4)));
+  auto read_scales = [&](int kb, float (&sc)[2][4]) __attribute__((always_inline)) {
+    const float* w0 = sc_lds + ((kb / SCW) & 1) * (SCW * 64) + (kb % SCW) * 64 + (2 * wm) * 8 + 4 * wn;
+    const v4f_t r0 = *reinterpret_cast<const v4f_t*>(w0);
+    const v4f_t r1 = *reinterpret_cast<const v4f_t*>(w0 + 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sc[2 + j] = w0[8 * SCW + (4 * wn + j) * SCW + kk];
+    for (int j = 0; j < 4; ++j) {
+      sc[0][j] = r0[j];
+      sc[1][j] = r1[j];
+    }
   };
 
   v4f acc[4][8];
@@ -181,7 +184,9 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 
   // ---- prologue: K-blocks 0 and 1 staged in LDS, K-block 2 in registers,
   // K-block 0's fragments in registers
-  load_scale_window(0);
+  // K = 0: no operand or scale is touched (the caller may pass null pointers);
+  // the accumulators stay zero.
+  if (KB > 0) load_scale_window(0);
   uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
   if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
   if (KB > 1) { load_stage(1, ra, rb); store_stage(1, ra, rb); }
@@ -201,20 +206,14 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // receives the K-block held in registers.  One barrier per iteration orders
   // the three.
   int sn = 1, sf = 2;  // stages (kb+1)%3 and (kb+2)%3, wave-uniform
-  float sc_cur[6];
-  read_scales(0, sc_cur);
+  // the scale products of the current K-block; those of the next are read
+  // right after the last promotion, into the same registers, so the barrier
+  // hides the LDS latency
+  float s_cur[2][4];
+  if (KB > 0) read_scales(0, s_cur);
   for (int kb = 0; kb < KB; ++kb) {
-    // next window of scales: written now, first read SCW iterations later
+    // next window of scale products: written now, first read SCW iterations later
     if (kb % SCW == 0 && kb + SCW < KB) load_scale_window(kb / SCW + 1);
-    // the scales of the next K-block, read one iteration ahead
-    float sc_nxt[6];
-    read_scales(kb + 1 < KB ? kb + 1 : kb, sc_nxt);
-    float s_cur[2][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      s_cur[0][j] = sc_cur[0] * sc_cur[2 + j];
-      s_cur[1][j] = sc_cur[1] * sc_cur[2 + j];
-    }
 
     // 32 sub-tile partials, j outer, so that each B fragment is dead after its
     // four uses and is refilled with the next K-block's; partials pass through
@@ -245,8 +244,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       }
       if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < 6; ++i) sc_cur[i] = sc_nxt[i];
+    read_scales(kb + 1 < KB ? kb + 1 : kb, s_cur);
     __syncthreads();
     sn = sn == 2 ? 0 : sn + 1;
     sf = sf == 2 ? 0 : sf + 1;
@@ -564,8 +562,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
 
   const int rounds = (KB + SWAVES - 1) / SWAVES;
   const int full_rounds = KB / SWAVES;
+  // K = 0: nothing is loaded (the caller may pass null pointers); zeros are stored.
+  if (KB > 0) {
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) issue(d);
+    for (int d = 0; d < D - 1; ++d) issue(d);
+  }
 
   for (int r = 0; r < rounds; ++r) {
     wait_vmcnt<(D - 2) * Cfg::OPS>();  // this wave's round-r loads have landed

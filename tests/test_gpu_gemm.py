@@ -106,10 +106,16 @@ def test_zero_blocks_and_empty_k():
     say("gemm zero blocks")
     c = gpu_gemm(qa, sa, qb, sb)
     assert np.all(c == 0)
-    say("gemm K=0")
-    c = gpu_gemm(np.zeros((70, 0), np.uint8), np.zeros((3, 0), np.float32), np.zeros((0, 64), np.uint8),
-                 np.zeros((0, 2), np.float32))
-    assert np.all(c == 0)
+    for m in (70, 5):  # tile kernel, small-M kernel
+        say(f"gemm K=0 M={m}")
+        c = gpu_gemm(np.zeros((m, 0), np.uint8), np.zeros((-(-m // 32), 0), np.float32),
+                     np.zeros((0, 64), np.uint8), np.zeros((0, 2), np.float32))
+        assert c.shape == (m, 64) and np.all(c == 0)
+    say("grouped K=0")
+    off = np.array([0, 32, 32, 96], np.int32)
+    c = gpu_grouped(np.zeros((96, 0), np.uint8), np.zeros((3, 0), np.float32), np.zeros((3, 0, 64), np.uint8),
+                    np.zeros((3, 0, 2), np.float32), off)
+    assert c.shape == (96, 64) and np.all(c == 0)
 
 
 def test_rows_independent_of_batch():
