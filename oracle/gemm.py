@@ -18,6 +18,10 @@ Grouped variant (DeepGEMM write-up, sections 4.1-4.2): consecutive row ranges
 [off[g], off[g+1]) of A are multiplied by their own B_g / sb_g; empty ranges
 produce nothing.
 
+K-major weights (section 6 passes the weight as [N, K] with scales
+[N/32, K/32]): ``gemm_ref_nt`` / ``grouped_gemm_ref_nt`` take B transposed;
+the product is the same definition with B[k, j] = Bt[j, k].
+
 Acceptance bound per element (the tolerance the GPU result is held to):
     |C - ref| <= 2**-8 * |ref| + 1e-6 * sum_k |a' b'|
 """
@@ -72,6 +76,19 @@ def gemm_ref_at(qa, sa, qb, sb, rows, cols):
     return a @ b, np.abs(a) @ np.abs(b)
 
 
+def gemm_ref_nt(qa, sa, qbt, sbt):
+    """K-major weights: qbt [N, K] with scales sbt [N/32, K/32] (the weight
+    layout of the DeepGEMM write-up's call interface, section 6).
+
+        C[i, j] = sum_k dec(A[i, k]) sa[i//32, k//32] * dec(Bt[j, k]) sbt[j//32, k//32]
+
+    Both operands are dequantized with their own grids (entry (r, c) uses
+    [r // 32, c // 32]) and contracted over K.  Returns (ref, absref)."""
+    a = dequantize(qa, sa)
+    bt = dequantize(qbt, sbt)
+    return a @ bt.T, np.abs(a) @ np.abs(bt).T
+
+
 def _check_offsets(offsets, M_total):
     off = np.asarray(offsets, dtype=np.int64)
     if off[0] != 0 or off[-1] != M_total or np.any(np.diff(off) < 0) or np.any(off % BLOCK):
@@ -91,6 +108,23 @@ def grouped_gemm_ref(qa, sa, qb, sb, offsets):
         if r1 == r0:
             continue
         r, ar = gemm_ref(qa[r0:r1], np.asarray(sa)[r0 // BLOCK:r1 // BLOCK], qb[g], sb[g])
+        ref[r0:r1] = r
+        absref[r0:r1] = ar
+    return ref, absref
+
+
+def grouped_gemm_ref_nt(qa, sa, qbt, sbt, offsets):
+    """qbt [G, N, K], sbt [G, N/32, K/32]; rows off[g]..off[g+1] use group g."""
+    qa = np.asarray(qa)
+    off = _check_offsets(offsets, qa.shape[0])
+    M, N = qa.shape[0], qbt.shape[1]
+    ref = np.zeros((M, N))
+    absref = np.zeros((M, N))
+    for g in range(len(off) - 1):
+        r0, r1 = off[g], off[g + 1]
+        if r1 == r0:
+            continue
+        r, ar = gemm_ref_nt(qa[r0:r1], np.asarray(sa)[r0 // BLOCK:r1 // BLOCK], qbt[g], sbt[g])
         ref[r0:r1] = r
         absref[r0:r1] = ar
     return ref, absref

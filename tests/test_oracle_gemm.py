@@ -3,8 +3,9 @@
 import numpy as np
 import pytest
 
-from oracle import (FINITE_E4M3_CODES, decode_e4m3, gemm_exact, gemm_ref, gemm_ref_at, grouped_gemm_ref,
-                    grouped_gemm_ref_at, tolerance_ok, tolerance_bound)
+from oracle import (FINITE_E4M3_CODES, decode_e4m3, gemm_exact, gemm_ref, gemm_ref_at, gemm_ref_nt,
+                    grouped_gemm_ref, grouped_gemm_ref_at, grouped_gemm_ref_nt, quantize_blocks, tolerance_ok,
+                    tolerance_bound)
 from oracle.exact import _int_units
 
 
@@ -126,6 +127,47 @@ def test_grouped_is_per_group_gemm():
     assert np.all(np.abs(r - ref[sel]) <= 1e-14 * absref[sel])
     with pytest.raises(ValueError):
         grouped_gemm_ref(qa, sa, qb, sb, np.array([0, 16, M]))
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 32, 64), (33, 64, 32), (32, 32, 32)])
+def test_k_major_reference_matches_exact_rational(M, N, K):
+    """gemm_ref_nt on Bt [N, K] against the exact rational product of the same
+    values laid out [K, N]; a square case so that a missing transpose or a
+    scale grid read the wrong way round cannot pass by shape."""
+    g = np.random.default_rng(M * 7 + N + K)
+    qa, qbt = _rand_codes(g, (M, K)), _rand_codes(g, (N, K))
+    sa, sbt = _rand_scales(g, (-(-M // 32), K // 32)), _rand_scales(g, (N // 32, K // 32))
+    ref, absref = gemm_ref_nt(qa, sa, qbt, sbt)
+    ex = np.vectorize(float)(gemm_exact(qa, sa, np.ascontiguousarray(qbt.T), np.ascontiguousarray(sbt.T)))
+    u = 2.0 ** -53
+    gam = (K + 2) * u / (1 - (K + 2) * u)
+    assert np.all(np.abs(ref - ex) <= gam * absref + 1e-300)
+
+
+def test_k_major_grouped_is_per_group():
+    g = np.random.default_rng(9)
+    G, K, N = 4, 64, 32
+    off = np.array([0, 32, 32, 96, 128], np.int32)
+    qa, sa = _rand_codes(g, (128, K)), _rand_scales(g, (4, K // 32))
+    qbt, sbt = _rand_codes(g, (G, N, K)), _rand_scales(g, (G, N // 32, K // 32))
+    ref, _ = grouped_gemm_ref_nt(qa, sa, qbt, sbt, off)
+    for gi in range(G):
+        r0, r1 = off[gi], off[gi + 1]
+        if r1 > r0:
+            ex = np.vectorize(float)(gemm_exact(qa[r0:r1], sa[r0 // 32:r1 // 32], qbt[gi].T, sbt[gi].T))
+            assert np.all(np.abs(ref[r0:r1] - ex) <= 1e-12 * np.abs(ex) + 1e-300)
+
+
+def test_quantizer_is_orientation_symmetric():
+    """A 32x32 block holds the same elements read row- or column-major, so
+    quantizing B^T gives the transposed codes and the transposed scale grid:
+    the K-major weight path needs no quantizer of its own."""
+    g = np.random.default_rng(10)
+    x = (g.standard_normal((96, 64)).astype(np.float32) * np.float32(0.02)).view(np.uint32)
+    bits = ((x + 0x7FFF + ((x >> 16) & 1)) >> 16).astype(np.uint16)
+    q, s = quantize_blocks(bits)
+    qt, st = quantize_blocks(np.ascontiguousarray(bits.T))
+    assert np.array_equal(qt, q.T) and np.array_equal(st, s.T)
 
 
 def test_tolerance_accepts_exact_and_rejects_outside():
