@@ -6,8 +6,9 @@ package loads nothing; the first call loads the library and raises
 ``Fp8bsError`` if it is missing.
 """
 
-_BINDING_NAMES = ("Fp8bsError", "quantize", "gemm", "grouped_gemm", "library_path", "load_library",
-                  "quantize_raw", "gemm_raw", "grouped_gemm_raw")
+_BINDING_NAMES = ("Fp8bsError", "quantize", "gemm", "grouped_gemm", "gemm_nt", "grouped_gemm_nt", "library_path",
+                  "load_library", "quantize_raw", "gemm_raw", "grouped_gemm_raw", "gemm_nt_raw",
+                  "grouped_gemm_nt_raw")
 
 __all__ = list(_BINDING_NAMES)
 

@@ -49,6 +49,10 @@ def load_library() -> ctypes.CDLL:
         lib.fp8bs_gemm.restype = ctypes.c_int
         lib.fp8bs_grouped_gemm.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, vp]
         lib.fp8bs_grouped_gemm.restype = ctypes.c_int
+        lib.fp8bs_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.fp8bs_gemm_nt.restype = ctypes.c_int
+        lib.fp8bs_grouped_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, vp]
+        lib.fp8bs_grouped_gemm_nt.restype = ctypes.c_int
         lib.fp8bs_status_str.argtypes = [ctypes.c_int]
         lib.fp8bs_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -96,6 +100,15 @@ def quantize_raw(x_ptr, rows, cols, q_ptr, s_ptr, stream=None) -> int:
 
 def gemm_raw(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream=None) -> int:
     return load_library().fp8bs_gemm(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream)
+
+
+def gemm_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) -> int:
+    return load_library().fp8bs_gemm_nt(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream)
+
+
+def grouped_gemm_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, off_ptr, G, c_ptr, M_total, N, K, stream=None) -> int:
+    return load_library().fp8bs_grouped_gemm_nt(a_ptr, sa_ptr, bt_ptr, sbt_ptr, off_ptr, G, c_ptr, M_total, N, K,
+                                                stream)
 
 
 def grouped_gemm_raw(a_ptr, sa_ptr, b_ptr, sb_ptr, off_ptr, G, c_ptr, M_total, N, K, stream=None) -> int:
@@ -164,4 +177,52 @@ def grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.T
     _same_device(a, sa, b, sb, offsets, out)
     _check(grouped_gemm_raw(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(offsets), G, _ptr(out), M, N, K,
                             _stream_ptr(a)))
+    return out
+
+
+def gemm_nt(a: torch.Tensor, sa: torch.Tensor, bt: torch.Tensor, sbt: torch.Tensor,
+            out: torch.Tensor | None = None):
+    """K-major weight: E4M3 a [M, K], sa [ceil(M/32), K/32], bt [N, K], sbt [N/32, K/32] -> bf16 [M, N]."""
+    _need(a, "a", E4M3_DTYPES, 2)
+    _need(bt, "bt", E4M3_DTYPES, 2)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sbt, "sbt", torch.float32, 2)
+    M, K = a.shape
+    N, K2 = bt.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if tuple(sa.shape) != ((M + BLOCK - 1) // BLOCK, K // BLOCK) or tuple(sbt.shape) != (N // BLOCK, K // BLOCK):
+        raise ValueError("scale grid shapes do not match the operands")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _same_device(a, sa, bt, sbt, out)
+    _check(gemm_nt_raw(_ptr(a), _ptr(sa), _ptr(bt), _ptr(sbt), _ptr(out), M, N, K, _stream_ptr(a)))
+    return out
+
+
+def grouped_gemm_nt(a: torch.Tensor, sa: torch.Tensor, bt: torch.Tensor, sbt: torch.Tensor, offsets: torch.Tensor,
+                    out: torch.Tensor | None = None):
+    """a [M_total, K], sa [M_total/32, K/32], bt [G, N, K], sbt [G, N/32, K/32], offsets int32 [G+1] on device."""
+    _need(a, "a", E4M3_DTYPES, 2)
+    _need(bt, "bt", E4M3_DTYPES, 3)
+    _need(sa, "sa", torch.float32, 2)
+    _need(sbt, "sbt", torch.float32, 3)
+    _need(offsets, "offsets", torch.int32, 1)
+    M, K = a.shape
+    G, N, K2 = bt.shape
+    if K2 != K or offsets.shape[0] != G + 1:
+        raise ValueError("shape mismatch between a, bt and offsets")
+    if tuple(sa.shape) != (M // BLOCK, K // BLOCK) or tuple(sbt.shape) != (G, N // BLOCK, K // BLOCK):
+        raise ValueError("scale grid shapes do not match the operands")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _same_device(a, sa, bt, sbt, offsets, out)
+    _check(grouped_gemm_nt_raw(_ptr(a), _ptr(sa), _ptr(bt), _ptr(sbt), _ptr(offsets), G, _ptr(out), M, N, K,
+                               _stream_ptr(a)))
     return out

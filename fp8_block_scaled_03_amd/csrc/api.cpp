@@ -66,8 +66,8 @@ fp8bs_status fp8bs_quantize(const void* x_bf16, int64_t rows, int64_t cols, void
   return from_hip(fp8bs::launch_quantize(x_bf16, rows, cols, q_e4m3, scales, (hipStream_t)stream));
 }
 
-fp8bs_status fp8bs_gemm(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16, int64_t M,
-                        int64_t N, int64_t K, void* stream) {
+static fp8bs_status gemm_common(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16,
+                                int64_t M, int64_t N, int64_t K, bool k_major_b, void* stream) {
   fp8bs_status st = check_gemm_dims(M, N, K);
   if (st != FP8BS_OK) return st;
   if (M == 0 || N == 0) return FP8BS_OK;
@@ -78,13 +78,14 @@ fp8bs_status fp8bs_gemm(const void* a, const float* sa, const void* b, const flo
   st = ensure_attributes();
   if (st != FP8BS_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (M <= fp8bs::SMALL_M_MAX) return from_hip(fp8bs::launch_gemm_smallm(a, sa, b, sb, c_bf16, M, N, K, s));
-  return from_hip(fp8bs::launch_gemm_tile(a, sa, b, sb, c_bf16, M, N, K, s));
+  if (M <= fp8bs::SMALL_M_MAX)
+    return from_hip(fp8bs::launch_gemm_smallm(a, sa, b, sb, c_bf16, M, N, K, k_major_b, s));
+  return from_hip(fp8bs::launch_gemm_tile(a, sa, b, sb, c_bf16, M, N, K, k_major_b, s));
 }
 
-fp8bs_status fp8bs_grouped_gemm(const void* a, const float* sa, const void* b, const float* sb,
-                                const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
-                                int64_t K, void* stream) {
+static fp8bs_status grouped_common(const void* a, const float* sa, const void* b, const float* sb,
+                                   const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
+                                   int64_t K, bool k_major_b, void* stream) {
   if (G < 1 || G > FP8BS_MAX_GROUPS) return FP8BS_EINVAL;
   fp8bs_status st = check_gemm_dims(M_total, N, K);
   if (st != FP8BS_OK) return st;
@@ -98,8 +99,30 @@ fp8bs_status fp8bs_grouped_gemm(const void* a, const float* sa, const void* b, c
     return FP8BS_EALIGN;
   st = ensure_attributes();
   if (st != FP8BS_OK) return st;
-  return from_hip(fp8bs::launch_gemm_grouped(a, sa, b, sb, offsets_dev, G, c_bf16, M_total, N, K,
+  return from_hip(fp8bs::launch_gemm_grouped(a, sa, b, sb, offsets_dev, G, c_bf16, M_total, N, K, k_major_b,
                                              (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_gemm(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16, int64_t M,
+                        int64_t N, int64_t K, void* stream) {
+  return gemm_common(a, sa, b, sb, c_bf16, M, N, K, false, stream);
+}
+
+fp8bs_status fp8bs_gemm_nt(const void* a, const float* sa, const void* bt, const float* sbt, void* c_bf16,
+                           int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_common(a, sa, bt, sbt, c_bf16, M, N, K, true, stream);
+}
+
+fp8bs_status fp8bs_grouped_gemm(const void* a, const float* sa, const void* b, const float* sb,
+                                const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
+                                int64_t K, void* stream) {
+  return grouped_common(a, sa, b, sb, offsets_dev, G, c_bf16, M_total, N, K, false, stream);
+}
+
+fp8bs_status fp8bs_grouped_gemm_nt(const void* a, const float* sa, const void* bt, const float* sbt,
+                                   const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
+                                   int64_t K, void* stream) {
+  return grouped_common(a, sa, bt, sbt, offsets_dev, G, c_bf16, M_total, N, K, true, stream);
 }
 
 }  // extern "C"

@@ -58,8 +58,8 @@ __device__ __forceinline__ int b_lds_off(int k, int chunk) {
 struct TileArgs {
   const uint8_t* a;   // rows of this problem start here (global row index 0)
   const float* sa;    // [ceil(M/32), KB]
-  const uint8_t* b;   // [K, N]
-  const float* sb;    // [KB, NB]
+  const uint8_t* b;   // [K, N], or [N, K] when the weight is K-major
+  const float* sb;    // [KB, NB], or [NB, KB] when the weight is K-major
   uint16_t* c;        // [.., N]
   int64_t N, K;
   int64_t row0;       // first row of the tile
@@ -68,6 +68,10 @@ struct TileArgs {
   int64_t sa_rows;    // number of scale rows (for clamping)
 };
 
+// BT: the weight is K-major (B^T, [N, K]); its rows are staged and read exactly
+// like rows of A (K-contiguous, no transposed LDS reads), and its scale grid is
+// [NB, KB].
+template <bool BT>
 __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem) {
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -82,20 +86,36 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 
   // ---- global -> register staging assignment
   const int a_row = t >> 1, a_half = t & 1;           // 16 E4M3 of A row a_row
-  const int b_row = t >> 4, b_chunk = t & 15;         // 16 E4M3 of B row b_row
   const int64_t ga_row = p.row0 + a_row;
   const bool a_ok = ga_row < p.row_end;
-  const bool b_ok = (p.col0 + b_chunk * 16) < N;
   const uint8_t* a_src = p.a + (a_ok ? ga_row : 0) * K + a_half * 16;
-  const uint8_t* b_src = p.b + (int64_t)b_row * N + (b_ok ? p.col0 + b_chunk * 16 : 0);
+  // B [K, N]: 16 E4M3 of K-row t>>4, 16-column chunk t&15.  B^T [N, K]: like A,
+  // 16 E4M3 of weight row (column of C) col0 + (t>>1), half t&1 of the K-block.
+  bool b_ok;
+  const uint8_t* b_src;
+  lds_u8* st_b;
+  lds_u8* st_b1;
+  if constexpr (BT) {
+    const int64_t gn = p.col0 + (t >> 1);
+    b_ok = gn < N;
+    b_src = p.b + (b_ok ? gn : 0) * K + (t & 1) * 16;
+    st_b = sB + a_lds_off(t >> 1, 2 * (t & 1));
+    st_b1 = sB + a_lds_off(t >> 1, 2 * (t & 1) + 1);
+  } else {
+    const int b_row = t >> 4, b_chunk = t & 15;
+    b_ok = (p.col0 + b_chunk * 16) < N;
+    b_src = p.b + (int64_t)b_row * N + (b_ok ? p.col0 + b_chunk * 16 : 0);
+    st_b = sB + b_lds_off(b_row, b_chunk);
+    st_b1 = st_b + 16;
+  }
   // LDS store addresses (stage 0); other stages add a compile-time offset
   lds_u8* const st_a0 = sA + a_lds_off(a_row, 2 * a_half);
   lds_u8* const st_a1 = sA + a_lds_off(a_row, 2 * a_half + 1);
-  lds_u8* const st_b = sB + b_lds_off(b_row, b_chunk);
 
   auto load_stage = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
     ra = a_ok ? *reinterpret_cast<const uint4*>(a_src + (int64_t)kb * 32) : make_uint4(0, 0, 0, 0);
-    rb = b_ok ? *reinterpret_cast<const uint4*>(b_src + (int64_t)kb * 32 * N) : make_uint4(0, 0, 0, 0);
+    const int64_t boff = BT ? (int64_t)kb * 32 : (int64_t)kb * 32 * N;
+    rb = b_ok ? *reinterpret_cast<const uint4*>(b_src + boff) : make_uint4(0, 0, 0, 0);
   };
   // `st` is the stage index (wave-uniform, 0..2)
   auto store_stage = [&](int st, uint4 ra, uint4 rb) __attribute__((always_inline)) {
@@ -108,7 +128,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     *(lds_v4u*)(st_a0 + soa) = v4u{a0.x, a0.y, a0.z, a0.w};
     *(lds_v4u*)(st_a1 + soa) = v4u{a1.x, a1.y, a1.z, a1.w};
     *(lds_v4u*)(st_b + sob) = v4u{b0.x, b0.y, b0.z, b0.w};
-    *(lds_v4u*)(st_b + sob + 16) = v4u{b1.x, b1.y, b1.z, b1.w};
+    *(lds_v4u*)(st_b1 + sob) = v4u{b1.x, b1.y, b1.z, b1.w};
   };
 
   // ---- fragment read addresses.  A: row wm*64 + i*16 + (lane&15), chunk lane>>4;
@@ -128,7 +148,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
     return *(lds_v8bf*)(rd_a + st * A_STAGE_BYTES + i * 1024);
   };
+  // B^T: weight row wn*128 + j*16 + (lane&15), chunk lane>>4, read like A
+  const lds_u8* const rd_bt = sB + a_lds_off(wn * 128 + fr_lo, fr_kc);
   auto read_b = [&](int st, int j) __attribute__((always_inline)) -> v8bf {
+    if constexpr (BT) {
+      typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
+      return *(lds_v8bf*)(rd_bt + st * B_STAGE_BYTES + j * 1024);
+    }
     const lds_u8* base = rd_b[j & 3] + st * B_STAGE_BYTES + (j >> 2) * 128;
     v4s h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base));
     v4s h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 4 * 512));
@@ -149,7 +175,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   int64_t sb_col = cb_tile + w_cb;
   sb_col = sb_col < NB ? sb_col : NB - 1;
   const float* const sa_src = p.sa + sa_row * KB;
-  const float* const sb_src = p.sb + sb_col;
+  const float* const sb_src = BT ? p.sb + sb_col * KB : p.sb + sb_col;
+  const int64_t sb_kstride = BT ? 1 : NB;
   auto load_scale_window = [&](int win) __attribute__((always_inline)) {
     float* dst = sc_lds + (win & 1) * (SCW * 64);
     float va[SCW / 8], vb[SCW / 8];
@@ -158,7 +185,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       int kk = win * SCW + w_k0 + 8 * i;
       kk = kk < KB ? kk : KB - 1;  // past the end: any valid block (never read)
       va[i] = sa_src[kk];
-      vb[i] = sb_src[(int64_t)kk * NB];
+      vb[i] = sb_src[(int64_t)kk * sb_kstride];
     }
 #pragma unroll
     for (int i = 0; i < SCW / 8; ++i) dst[(w_k0 + 8 * i) * 64 + w_rb * 8 + w_cb] = va[i] * vb[i];
@@ -299,6 +326,7 @@ __device__ __forceinline__ void tile_coords(int64_t id, int64_t n_tiles, int64_t
   tn = r / gm;
 }
 
+template <bool BT>
 __global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __restrict__ a,
                                                              const float* __restrict__ sa,
                                                              const uint8_t* __restrict__ b,
@@ -326,13 +354,14 @@ __global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __re
   p.row_end = M;
   p.col0 = tn * TBN;
   p.sa_rows = (M + 31) >> 5;
-  tile_body(p, smem);
+  tile_body<BT>(p, smem);
 }
 
 // Grouped: the grid is an upper bound on the tile count, (M_total/256 + G) x
 // tiles_n; each workgroup walks the device-side offsets to find its group and
 // M-tile, and leaves if it has none.  Shapes never enter launch arguments that
 // change with the group sizes (DeepGEMM write-up, section 4.3).
+template <bool BT>
 __global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* __restrict__ a,
                                                                 const float* __restrict__ sa,
                                                                 const uint8_t* __restrict__ b,
@@ -378,7 +407,7 @@ __global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* _
   p.row_end = end;
   p.col0 = tn * TBN;
   p.sa_rows = M_total >> 5;
-  tile_body(p, smem);
+  tile_body<BT>(p, smem);
 }
 
 // ------------------------------------------------------------------------------------
@@ -594,73 +623,304 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
 }
 
 // ------------------------------------------------------------------------------------
+// small-M kernel, K-major weight (B^T [N, K], scales [NB, KB])
+// ------------------------------------------------------------------------------------
+// The workgroup's W = 32*NCB columns of C are W contiguous rows of B^T, so each
+// round streams W rows x 256 bytes (eight K-blocks) and every row is read as
+// whole 256-byte runs.  Round buffer layout (one per ring slot): the W weight
+// rows, then the 32*ACH A rows, each 256 bytes with 16-byte piece p of row r
+// holding global piece p ^ (r & 15) (the fragment reads of sixteen rows at one
+// K offset then hit sixteen bank groups), then eight 256-byte scale records
+// (record q: sa of row-blocks 0 and 1, sb of the NCB column blocks, for K-block
+// 8r+q).  Every wave issues NCB 1 KB weight loads, ACH 1 KB A loads and one
+// scale record per round.
+template <int MT, int NCB>
+struct SmallMNtCfg {
+  static constexpr int W = 32 * NCB;
+  static constexpr int ACH = (MT + 1) / 2;
+  static constexpr int A_OFF = W * 256;
+  static constexpr int SC_OFF = A_OFF + 32 * ACH * 256;
+  static constexpr int SLOT = SC_OFF + SWAVES * 256;
+  static constexpr int D_FIT = SMALL_LDS_BUDGET / SLOT;
+  static constexpr int D = D_FIT > 6 ? 6 : D_FIT;
+  static constexpr int LDS = D * SLOT;
+  static constexpr int OPS = NCB + ACH + 1;
+  static constexpr int CS = 2 * NCB;
+  static constexpr int RG = SWAVES / CS;
+  static constexpr int TPW = (MT + RG - 1) / RG;
+  static_assert(D >= 3, "ring too shallow");
+  static_assert(LDS <= SMALL_LDS_BUDGET, "LDS budget");
+  static_assert((D - 2) * OPS < 64, "vmcnt range");
+};
+
+template <int MT, int NCB>
+__global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t* __restrict__ a,
+                                                                  const float* __restrict__ sa,
+                                                                  const uint8_t* __restrict__ bt,
+                                                                  const float* __restrict__ sbt,
+                                                                  uint16_t* __restrict__ c, int64_t M, int64_t N,
+                                                                  int64_t K) {
+  using Cfg = SmallMNtCfg<MT, NCB>;
+  constexpr int D = Cfg::D, W = Cfg::W;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const int KB = (int)(K >> 5);
+  const int64_t n_slices = N / W;
+  const int64_t slice = blockIdx.x;
+  const int64_t n0 = slice * W;
+  const int cb0 = (int)(n0 >> 5);
+
+  // ---- this wave's direct loads for round r
+  // weight piece i: rows 4*(w*NCB + i) .. +3; lane l -> row 4*(w*NCB+i) + l/16, LDS piece l%16
+  const int lp = lane & 15;
+  const uint8_t* b_row[NCB];
+  int b_g[NCB];
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const int r = 4 * (w * NCB + i) + (lane >> 4);
+    b_row[i] = bt + (n0 + r) * K;
+    b_g[i] = lp ^ (r & 15);
+  }
+  // A piece ch: rows 4*(w + 8*ch) .. +3 (rows past M read row M-1).  A piece
+  // whose four rows all lie past M is not loaded at all: an MFMA output row
+  // depends only on its own A row, and rows past M are never stored, so
+  // whatever their LDS bytes hold cannot reach C.  a_live (wave-uniform) counts
+  // this wave's loaded pieces; they are the first a_live values of ch.
+  const uint8_t* a_row[Cfg::ACH];
+  int a_g[Cfg::ACH];
+  int a_live = 0;
+#pragma unroll
+  for (int ch = 0; ch < Cfg::ACH; ++ch) {
+    const int r = 4 * (w + 8 * ch) + (lane >> 4);
+    const int64_t rr = r < M ? r : M - 1;
+    a_row[ch] = a + rr * K;
+    a_g[ch] = lp ^ (r & 15);
+    a_live += 4 * (w + 8 * ch) < M ? 1 : 0;
+  }
+  const int nrb = (int)((M + 31) >> 5);
+  const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
+  const float* const sc_src = lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sbt + (int64_t)(cb0 + sbj) * KB;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
+
+  // byte offset in a row of global piece g of round r; pieces of K-blocks past
+  // the end re-read the last K-block (their results are never used)
+  auto koff = [&](int r, int g) __attribute__((always_inline)) -> int64_t {
+    int kb = r * SWAVES + (g >> 1);
+    kb = kb < KB ? kb : KB - 1;
+    return (int64_t)kb * 32 + (g & 1) * 16;
+  };
+  auto issue = [&](int r) __attribute__((always_inline)) {
+    const uint32_t sl = ring + (r % D) * Cfg::SLOT;
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) dma16(b_row[i] + koff(r, b_g[i]), sl + (w * NCB + i) * 1024);
+#pragma unroll
+    for (int ch = 0; ch < Cfg::ACH; ++ch)
+      if (ch < a_live) dma16(a_row[ch] + koff(r, a_g[ch]), sl + Cfg::A_OFF + (w + 8 * ch) * 1024);
+    int kc = r * SWAVES + w;
+    kc = kc < KB ? kc : KB - 1;
+    dma4(sc_src + kc, sl + Cfg::SC_OFF + w * 256);
+  };
+
+  // ---- ownership (as in the [K, N] kernel): 16-column sub-tile cs, row tiles rg, rg + RG, ...
+  const int cs = w % Cfg::CS;
+  const int rg = Cfg::RG == 1 ? 0 : w / Cfg::CS;
+  const int own_cb = cs >> 1;
+  const bool owns = rg < MT;
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
+    const int i = rg + t * Cfg::RG;
+    return i < MT ? i : MT - 1;
+  };
+  v4f acc[Cfg::TPW];
+#pragma unroll
+  for (int t = 0; t < Cfg::TPW; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // fragment of K-block q: lane l reads row (16*x + (l&15)), bytes 32q + 8*(l>>4):
+  // piece 2q + (l>>5), half (l>>4)&1; row & 15 = l & 15 for every such row
+  const int fr_half = ((lane >> 4) & 1) * 8, fr_hi = lane >> 5;
+  auto frag_off = [&](int row, int q) __attribute__((always_inline)) {
+    return row * 256 + 16 * ((2 * q + fr_hi) ^ (lane & 15)) + fr_half;
+  };
+
+  auto compute = [&](int slot, int nkb, auto FULL_) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(FULL_)::value;
+    const unsigned char* sl = smem + slot * Cfg::SLOT;
+    v2i braw[SWAVES];
+    v2i araw[SWAVES][Cfg::TPW];
+    float sbv[SWAVES], sav[SWAVES][2];
+#pragma unroll
+    for (int q = 0; q < SWAVES; ++q) {
+      braw[q] = *reinterpret_cast<const v2i*>(sl + frag_off(16 * cs + (lane & 15), q));
+#pragma unroll
+      for (int t = 0; t < Cfg::TPW; ++t)
+        araw[q][t] = *reinterpret_cast<const v2i*>(sl + Cfg::A_OFF + frag_off(16 * tile_of(t) + (lane & 15), q));
+      const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF + q * 256);
+      sav[q][0] = scr[0];
+      sav[q][1] = scr[1];
+      sbv[q] = scr[2 + own_cb];
+    }
+#pragma unroll
+    for (int q = 0; q < SWAVES; ++q) {
+      const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
+#pragma unroll
+      for (int t = 0; t < Cfg::TPW; ++t) {
+        const v4f p = mfma_partial(e4m3x8_to_bf16x8(araw[q][t]), bfrag);
+        const float sc = sav[q][tile_of(t) >> 1] * sbv[q];
+        if (FULL || q < nkb) promote(acc[t], p, sc);
+      }
+    }
+  };
+
+  const int rounds = (KB + SWAVES - 1) / SWAVES;
+  const int full_rounds = KB / SWAVES;
+  if (KB > 0) {
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) issue(d);
+  }
+  for (int r = 0; r < rounds; ++r) {
+    // this wave's round-r loads have landed: NCB + a_live + 1 loads per round
+    constexpr int LB = (D - 2) * (NCB + 1);
+    if (a_live == 0) wait_vmcnt<LB>();
+    else if (a_live == 1) wait_vmcnt<LB + (D - 2)>();
+    else wait_vmcnt<LB + 2 * (D - 2)>();
+    lds_barrier();                     // ... and everyone else's; round r-1's slot is free
+    issue(r + D - 1);                  // refill the slot that round r-1 used
+    if (owns) {
+      if (r < full_rounds) compute(r % D, SWAVES, std::true_type{});
+      else compute(r % D, KB - r * SWAVES, std::false_type{});
+    }
+  }
+  wait_vmcnt<0>();
+  (void)n_slices;
+
+  const int col = (int)n0 + cs * 16 + (lane & 15);
+#pragma unroll
+  for (int t = 0; t < Cfg::TPW; ++t) {
+    const int i = rg + t * Cfg::RG;
+    if (owns && i < MT) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
+        if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
 hipError_t launch_gemm_tile(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
-                            int64_t N, int64_t K, hipStream_t stream) {
+                            int64_t N, int64_t K, bool k_major_b, hipStream_t stream) {
   const int64_t tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + TBN - 1) / TBN;
   const int64_t n_tiles = tiles_m * tiles_n;
   const int remap = (n_tiles % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(gemm_tile_kernel, dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
-                     (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
+  if (k_major_b)
+    hipLaunchKernelGGL(gemm_tile_kernel<true>, dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                       (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
+  else
+    hipLaunchKernelGGL(gemm_tile_kernel<false>, dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                       (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped(const void* a, const float* sa, const void* b, const float* sb,
                                const int32_t* offsets, int G, void* c, int64_t M_total, int64_t N, int64_t K,
-                               hipStream_t stream) {
+                               bool k_major_b, hipStream_t stream) {
   const int64_t tiles_n = (N + TBN - 1) / TBN;
   const int64_t tiles_m_max = M_total / TBM + G;  // sum over groups of ceil(M_g / 256)
   const int64_t grid = tiles_m_max * tiles_n;
-  hipLaunchKernelGGL(gemm_grouped_kernel, dim3((unsigned)grid), dim3(TTHREADS), TILE_LDS_BYTES, stream,
-                     (const uint8_t*)a, sa, (const uint8_t*)b, sb, offsets, G, (uint16_t*)c, M_total, N, K, tiles_n);
+  if (k_major_b)
+    hipLaunchKernelGGL(gemm_grouped_kernel<true>, dim3((unsigned)grid), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                       (const uint8_t*)a, sa, (const uint8_t*)b, sb, offsets, G, (uint16_t*)c, M_total, N, K, tiles_n);
+  else
+    hipLaunchKernelGGL(gemm_grouped_kernel<false>, dim3((unsigned)grid), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                       (const uint8_t*)a, sa, (const uint8_t*)b, sb, offsets, G, (uint16_t*)c, M_total, N, K, tiles_n);
   return hipGetLastError();
 }
 
-// Column-slice width for the small-M kernel: 128-byte slices read whole cache
-// lines of B, but the grid must still cover most of the 256 CUs.
+// Column-slice width for the small-M kernel, [K, N] weight: 128-byte slices
+// read whole cache lines of B, but the grid must still cover most of the 256 CUs.
 int smallm_ncb(int64_t N) {
   if (N % 128 == 0 && N / 128 >= 192) return 4;
   if (N % 64 == 0 && N / 64 >= 192) return 2;
   return 1;
 }
 
-template <int MT, int NCB>
-static void launch_smallm_t(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  using Cfg = SmallMCfg<MT, NCB>;
-  hipLaunchKernelGGL((gemm_smallm_kernel<MT, NCB>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS, stream,
-                     a, sa, b, sb, c, M, N, K);
+// K-major weight: every slice streams whole rows whatever its width, so the
+// width only balances the grid over the 256 CUs (the fraction of the last wave
+// of workgroups that is busy); ties go to the wider slice.
+int smallm_nt_ncb(int64_t N) {
+  int best = 1;
+  double best_fill = -1.0;
+  for (int ncb : {4, 2, 1}) {
+    const int64_t w = 32 * ncb;
+    if (N % w) continue;
+    const int64_t g = N / w;
+    const double fill = (double)g / (double)(((g + 255) / 256) * 256);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = ncb;
+    }
+  }
+  return best;
 }
 
-template <int NCB>
+template <int MT, int NCB, bool NT>
+static void launch_smallm_t(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if constexpr (NT) {
+    using Cfg = SmallMNtCfg<MT, NCB>;
+    hipLaunchKernelGGL((gemm_smallm_nt_kernel<MT, NCB>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
+                       stream, a, sa, b, sb, c, M, N, K);
+  } else {
+    using Cfg = SmallMCfg<MT, NCB>;
+    hipLaunchKernelGGL((gemm_smallm_kernel<MT, NCB>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
+                       stream, a, sa, b, sb, c, M, N, K);
+  }
+}
+
+template <int NCB, bool NT>
 static void launch_smallm_n(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   switch ((int)((M + 15) / 16)) {
-    case 1: launch_smallm_t<1, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
-    case 2: launch_smallm_t<2, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
-    case 3: launch_smallm_t<3, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
-    default: launch_smallm_t<4, NCB>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 1: launch_smallm_t<1, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 2: launch_smallm_t<2, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 3: launch_smallm_t<3, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
+    default: launch_smallm_t<4, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
   }
 }
 
 hipError_t launch_gemm_smallm(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
-                              int64_t N, int64_t K, hipStream_t stream) {
+                              int64_t N, int64_t K, bool k_major_b, hipStream_t stream) {
   const uint8_t* a8 = (const uint8_t*)a;
   const uint8_t* b8 = (const uint8_t*)b;
   uint16_t* c16 = (uint16_t*)c;
-  switch (smallm_ncb(N)) {
-    case 4: launch_smallm_n<4>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-    case 2: launch_smallm_n<2>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-    default: launch_smallm_n<1>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+  if (k_major_b) {
+    switch (smallm_nt_ncb(N)) {
+      case 4: launch_smallm_n<4, true>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+      case 2: launch_smallm_n<2, true>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+      default: launch_smallm_n<1, true>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+    }
+  } else {
+    switch (smallm_ncb(N)) {
+      case 4: launch_smallm_n<4, false>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+      case 2: launch_smallm_n<2, false>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+      default: launch_smallm_n<1, false>(a8, sa, b8, sb, c16, M, N, K, stream); break;
+    }
   }
   return hipGetLastError();
 }
 
 template <int MT, int NCB>
 static hipError_t set_smallm_attr() {
-  return hipFuncSetAttribute((const void*)gemm_smallm_kernel<MT, NCB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             SmallMCfg<MT, NCB>::LDS);
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_smallm_kernel<MT, NCB>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, SmallMCfg<MT, NCB>::LDS);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_smallm_nt_kernel<MT, NCB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             SmallMNtCfg<MT, NCB>::LDS);
 }
 
 template <int NCB>
@@ -673,12 +933,12 @@ static hipError_t set_smallm_attrs() {
 }
 
 hipError_t set_gemm_attributes() {
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_tile_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     TILE_LDS_BYTES);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)gemm_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          TILE_LDS_BYTES);
-  if (e != hipSuccess) return e;
+  const void* tiles[4] = {(const void*)gemm_tile_kernel<false>, (const void*)gemm_tile_kernel<true>,
+                          (const void*)gemm_grouped_kernel<false>, (const void*)gemm_grouped_kernel<true>};
+  hipError_t e;
+  for (const void* f : tiles)
+    if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, TILE_LDS_BYTES)) != hipSuccess)
+      return e;
   if ((e = set_smallm_attrs<1>()) != hipSuccess) return e;
   if ((e = set_smallm_attrs<2>()) != hipSuccess) return e;
   return set_smallm_attrs<4>();

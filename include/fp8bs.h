@@ -103,6 +103,31 @@ fp8bs_status fp8bs_grouped_gemm(const void* a, const float* sa, const void* b, c
                                 const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
                                 int64_t K, void* stream);
 
+/*
+ * fp8bs_gemm_nt - fp8bs_gemm with the weight K-major, the layout of the
+ *   call interface in [DG 6] (weight [N, K], its scales [N/32, K/32]):
+ *     C[i,j] = sum_kb  sa[i/32, kb] * sbt[j/32, kb] * sum_{k in kb} A[i,k] Bt[j,k]
+ *   with the same per-element recipe as fp8bs_gemm, so every element is
+ *   bitwise equal to fp8bs_gemm on the transposed weight.  fp8bs_quantize of
+ *   the [N, K] bf16 weight gives exactly the transposed codes and scale grid of
+ *   quantizing its [K, N] transpose (blocks are 32x32 either way).
+ *   a   [M, K] E4M3, 16-byte aligned      sa  [ceil(M/32), K/32] fp32
+ *   bt  [N, K] E4M3, 16-byte aligned      sbt [N/32, K/32] fp32
+ *   c   [M, N] bf16 out, 16-byte aligned
+ *   Checks, errors and K == 0 as for fp8bs_gemm.
+ */
+fp8bs_status fp8bs_gemm_nt(const void* a, const float* sa, const void* bt, const float* sbt, void* c_bf16,
+                           int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * fp8bs_grouped_gemm_nt - fp8bs_grouped_gemm with K-major weights [DG 4.1-4.2, 6]:
+ *   bt [G, N, K] E4M3, sbt [G, N/32, K/32] fp32; everything else (offsets on
+ *   the device, empty ranges, untouched rows, checks) as fp8bs_grouped_gemm.
+ */
+fp8bs_status fp8bs_grouped_gemm_nt(const void* a, const float* sa, const void* bt, const float* sbt,
+                                   const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
+                                   int64_t K, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8bs_status_str(fp8bs_status status);
 

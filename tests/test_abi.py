@@ -23,7 +23,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = _declared_functions()
-    assert names == ["fp8bs_gemm", "fp8bs_grouped_gemm", "fp8bs_quantize", "fp8bs_status_str"]
+    assert names == ["fp8bs_gemm", "fp8bs_gemm_nt", "fp8bs_grouped_gemm", "fp8bs_grouped_gemm_nt", "fp8bs_quantize",
+                     "fp8bs_status_str"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -69,8 +70,19 @@ def test_gemm_argument_checks():
     assert g(A16, A4, A16, A4, A16, 4, 64, (1 << 30) + 32) == ESHAPE
 
 
-def test_grouped_argument_checks():
-    g = binding.grouped_gemm_raw
+@pytest.mark.parametrize("g", [binding.gemm_raw, binding.gemm_nt_raw])
+def test_gemm_argument_checks_both_layouts(g):
+    assert g(A16, A4, A16, A4, A16, 0, 64, 64) == OK
+    assert g(A16, A4, A16, A4, A16, 4, 64, 48) == ESHAPE
+    assert g(A16, A4, A16, A4, A16, 4, 40, 64) == ESHAPE
+    assert g(A16, A4, None, A4, A16, 4, 64, 64) == EINVAL
+    assert g(A16, A4, A16, None, A16, 4, 64, 64) == EINVAL
+    assert g(A16, A4, A16 + 8, A4, A16, 4, 64, 64) == EALIGN
+    assert g(A16, A4, A16, A4 + 1, A16, 4, 64, 64) == EALIGN
+
+
+@pytest.mark.parametrize("g", [binding.grouped_gemm_raw, binding.grouped_gemm_nt_raw])
+def test_grouped_argument_checks(g):
     assert g(A16, A4, A16, A4, A4, 0, A16, 64, 64, 64) == EINVAL      # G < 1
     assert g(A16, A4, A16, A4, A4, 1025, A16, 64, 64, 64) == EINVAL   # G > max
     assert g(A16, A4, A16, A4, None, 2, A16, 64, 64, 64) == EINVAL    # no offsets
