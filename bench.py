@@ -207,6 +207,58 @@ def main():
             del a64, db, q64, s64, dqb, dsb
         detail["decode_small_m"] = decode
 
+        # the same sweep with the weight K-major (B^T [N, K], the layout of the
+        # pages' call interface): each workgroup streams whole weight rows
+        decode_nt = []
+        for n_dec in (8192, 28672):
+            dwl = W.decode(64, n_dec)
+            a64 = to_dev_bf16(dwl.a_bits())
+            dbt = to_dev_bf16(np.ascontiguousarray(dwl.b_bits().T))
+            q64, s64 = fp8bs.quantize(a64)
+            dqbt, dsbt = fp8bs.quantize(dbt)
+            for m in (1, 8, 32, 64):
+                dqa, dsa = q64[:m].contiguous(), s64[:(m + 31) // 32].contiguous()
+                dc = torch.empty((m, n_dec), dtype=torch.bfloat16, device=dev)
+                fn = (lambda dqa=dqa, dsa=dsa, dc=dc: fp8bs.gemm_nt(dqa, dsa, dqbt, dsbt, out=dc))
+                for _ in range(3):
+                    fn()
+                d_med, d_min, d_avg = time_launch(fn, reps)
+                nbytes = m * dwl.K + dwl.K * n_dec + 4 * ((m + 31) // 32) * (dwl.K // 32) \
+                    + 4 * (dwl.K // 32) * (n_dec // 32) + 2 * m * n_dec
+                decode_nt.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
+                                  "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            del a64, dbt, q64, s64, dqbt, dsbt
+        detail["decode_small_m_k_major_weight"] = decode_nt
+
+        # prefill M = K = 8192, N = 28672 and the grouped workload (GEMM only)
+        pwl = W.prefill(28672)
+        pqa, psa = fp8bs.quantize(to_dev_bf16(pwl.a_bits()))
+        pqb, psb = fp8bs.quantize(to_dev_bf16(pwl.b_bits()))
+        pc = torch.empty((pwl.M, pwl.N), dtype=torch.bfloat16, device=dev)
+        pfn = lambda: fp8bs.gemm(pqa, psa, pqb, psb, out=pc)
+        pfn()
+        p_med, _, _ = time_launch(pfn, 10)
+        detail["prefill_M8192_K8192_N28672"] = {"median_ms": round(p_med, 4),
+                                                "tflops": round(pwl.flops() / (p_med * 1e-3) / 1e12, 1)}
+        del pqa, psa, pqb, psb, pc
+        gwl = W.grouped()
+        off = gwl.offsets()
+        gqa, gsa = fp8bs.quantize(to_dev_bf16(gwl.a_bits()))
+        gqb2, gsb2 = fp8bs.quantize(to_dev_bf16(gwl.b_bits().reshape(gwl.groups * gwl.K, gwl.N)))
+        gqb = gqb2.view(gwl.groups, gwl.K, gwl.N)
+        gsb = gsb2.view(gwl.groups, gwl.K // 32, gwl.N // 32)
+        goff = torch.from_numpy(off).to(dev)
+        gc = torch.empty((gwl.M, gwl.N), dtype=torch.bfloat16, device=dev)
+        gfn = lambda: fp8bs.grouped_gemm(gqa, gsa, gqb, gsb, goff, out=gc)
+        gfn()
+        g_med2, _, _ = time_launch(gfn, 10)
+        live = int(np.count_nonzero(np.diff(off)))
+        detail["grouped_G16_M8192_K7168_N4096"] = {"median_ms": round(g_med2, 4),
+                                                   "tflops": round(gwl.flops() / (g_med2 * 1e-3) / 1e12, 1),
+                                                   "live_groups": live}
+        del gqa, gsa, gqb2, gsb2, gc
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl)
