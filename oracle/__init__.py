@@ -26,16 +26,18 @@ itself; no function here is "parity unpinned".
 
 from .minifloat import Minifloat, E4M3FN, FP16, BF16
 from .e4m3 import decode_e4m3, encode_e4m3, FINITE_E4M3_CODES
-from .quantize import quantize_blocks, bf16_bits_to_f32, BLOCK
-from .gemm import (dequantize, gemm_ref, gemm_ref_at, gemm_ref_nt, grouped_gemm_ref, grouped_gemm_ref_at,
-                   grouped_gemm_ref_nt, tolerance_ok, tolerance_bound, bf16_bits_to_f64)
+from .quantize import quantize_blocks, quantize_token_groups, bf16_bits_to_f32, BLOCK
+from .gemm import (dequantize, dequantize_token_groups, gemm_ref, gemm_ref_at, gemm_ref_nt, gemm_ref_tg,
+                   gemm_ref_tg_nt, grouped_gemm_ref, grouped_gemm_ref_at, grouped_gemm_ref_nt, tolerance_ok,
+                   tolerance_bound, bf16_bits_to_f64)
 from .exact import gemm_exact
 
 __all__ = [
     "Minifloat", "E4M3FN", "FP16", "BF16",
     "decode_e4m3", "encode_e4m3", "FINITE_E4M3_CODES",
-    "quantize_blocks", "bf16_bits_to_f32", "BLOCK",
-    "dequantize", "gemm_ref", "gemm_ref_at", "gemm_ref_nt", "grouped_gemm_ref", "grouped_gemm_ref_at",
+    "quantize_blocks", "quantize_token_groups", "bf16_bits_to_f32", "BLOCK",
+    "dequantize", "dequantize_token_groups", "gemm_ref", "gemm_ref_at", "gemm_ref_nt", "gemm_ref_tg",
+    "gemm_ref_tg_nt", "grouped_gemm_ref", "grouped_gemm_ref_at",
     "grouped_gemm_ref_nt",
     "tolerance_ok", "tolerance_bound", "bf16_bits_to_f64",
     "gemm_exact",

@@ -22,6 +22,10 @@ K-major weights (section 6 passes the weight as [N, K] with scales
 [N/32, K/32]): ``gemm_ref_nt`` / ``grouped_gemm_ref_nt`` take B transposed;
 the product is the same definition with B[k, j] = Bt[j, k].
 
+Per-token-group activation scales (``gemm_ref_tg``, ``gemm_ref_tg_nt``): A's
+scale grid is [M, K/32], one scale per row and 32 columns; the product is the
+same definition with sa[i // 32, k // 32] replaced by sa_rows[i, k // 32].
+
 Acceptance bound per element (the tolerance the GPU result is held to):
     |C - ref| <= 2**-8 * |ref| + 1e-6 * sum_k |a' b'|
 """
@@ -85,6 +89,36 @@ def gemm_ref_nt(qa, sa, qbt, sbt):
     Both operands are dequantized with their own grids (entry (r, c) uses
     [r // 32, c // 32]) and contracted over K.  Returns (ref, absref)."""
     a = dequantize(qa, sa)
+    bt = dequantize(qbt, sbt)
+    return a @ bt.T, np.abs(a) @ np.abs(bt).T
+
+
+def dequantize_token_groups(q, s):
+    """A' = dec(q) * s expanded along columns: entry (r, c) uses s[r, c // 32]
+    (per-token groups of 1 x 32; s is [R, C/32])."""
+    q = np.asarray(q, dtype=np.uint8)
+    R, C = q.shape
+    s = np.asarray(s, dtype=np.float64)
+    if s.shape != (R, C // BLOCK):
+        raise ValueError(f"token-group scales {s.shape} do not match operand {q.shape}")
+    return decode_e4m3(q) * np.repeat(s, BLOCK, axis=1)
+
+
+def gemm_ref_tg(qa, sa_rows, qb, sb):
+    """Activations with per-token-group scales sa_rows [M, K/32], weight
+    B [K, N] with 32x32 block scales sb [K/32, N/32]:
+
+        C[i, j] = sum_k dec(A[i, k]) sa_rows[i, k//32] * dec(B[k, j]) sb[k//32, j//32]
+
+    Returns (ref, absref)."""
+    a = dequantize_token_groups(qa, sa_rows)
+    b = dequantize(qb, sb)
+    return a @ b, np.abs(a) @ np.abs(b)
+
+
+def gemm_ref_tg_nt(qa, sa_rows, qbt, sbt):
+    """As ``gemm_ref_tg`` with the weight K-major: qbt [N, K], sbt [N/32, K/32]."""
+    a = dequantize_token_groups(qa, sa_rows)
     bt = dequantize(qbt, sbt)
     return a @ bt.T, np.abs(a) @ np.abs(bt).T
 

@@ -62,3 +62,37 @@ def quantize_blocks(x_bits):
         qb[:, ~nz, :] = 0x00
         q[r0:r1] = qb.reshape(r1 - r0, C)
     return q, s
+
+
+def quantize_token_groups(x_bits):
+    """Per-token groups of 1 row x 32 columns (test oracle only).
+
+    The activation-side granularity that the determinism article's RMSNorm
+    part (三, section 2, the vLLM table) lists for a norm fused with FP8
+    quantization: one scale per token (row) and group of columns.  The group
+    width is 32 here, matching the 32-deep K-blocks of the weight's 32x32
+    scales.  Per group, the element rule of the block quantizer (DeepGEMM
+    write-up, sections 2.1 and 5.2): amax = max |x| over the group's 32
+    values, s = fp32(amax / 448), each code = E4M3(fp32(x / s)) (round half to
+    even, saturating at +-448, sign kept), an all-zero group gets s = 0 and
+    0x00 codes.
+
+    x_bits: uint16 bf16 patterns [R, C], C % 32 == 0.
+    Returns (q uint8 [R, C], s float32 [R, C/32]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    if x_bits.ndim != 2:
+        raise ValueError("quantize_token_groups takes a 2-D matrix")
+    R, C = x_bits.shape
+    if C % BLOCK:
+        raise ValueError("column count must be a multiple of 32")
+    ncb = C // BLOCK
+    xg = bf16_bits_to_f32(x_bits).reshape(R, ncb, BLOCK)
+    amax = np.abs(xg).max(axis=2).astype(np.float32)                   # [R, ncb]
+    sc = (amax / E4M3_MAX).astype(np.float32)
+    nz = sc != 0
+    t = np.zeros_like(xg)
+    t[nz] = (xg[nz] / sc[nz][:, None]).astype(np.float32)
+    q = encode_e4m3(t)
+    q[~nz] = 0x00
+    return q.reshape(R, C), sc
