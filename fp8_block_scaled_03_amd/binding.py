@@ -51,6 +51,12 @@ def load_library() -> ctypes.CDLL:
         lib.fp8bs_grouped_gemm.restype = ctypes.c_int
         lib.fp8bs_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
         lib.fp8bs_gemm_nt.restype = ctypes.c_int
+        lib.fp8bs_quantize_tg.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.fp8bs_quantize_tg.restype = ctypes.c_int
+        lib.fp8bs_gemm_tg.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.fp8bs_gemm_tg.restype = ctypes.c_int
+        lib.fp8bs_gemm_tg_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.fp8bs_gemm_tg_nt.restype = ctypes.c_int
         lib.fp8bs_grouped_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, vp]
         lib.fp8bs_grouped_gemm_nt.restype = ctypes.c_int
         lib.fp8bs_status_str.argtypes = [ctypes.c_int]
@@ -100,6 +106,18 @@ def quantize_raw(x_ptr, rows, cols, q_ptr, s_ptr, stream=None) -> int:
 
 def gemm_raw(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream=None) -> int:
     return load_library().fp8bs_gemm(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream)
+
+
+def quantize_tg_raw(x_ptr, rows, cols, q_ptr, s_ptr, stream=None) -> int:
+    return load_library().fp8bs_quantize_tg(x_ptr, rows, cols, q_ptr, s_ptr, stream)
+
+
+def gemm_tg_raw(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream=None) -> int:
+    return load_library().fp8bs_gemm_tg(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream)
+
+
+def gemm_tg_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) -> int:
+    return load_library().fp8bs_gemm_tg_nt(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream)
 
 
 def gemm_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) -> int:
@@ -226,3 +244,58 @@ def grouped_gemm_nt(a: torch.Tensor, sa: torch.Tensor, bt: torch.Tensor, sbt: to
     _check(grouped_gemm_nt_raw(_ptr(a), _ptr(sa), _ptr(bt), _ptr(sbt), _ptr(offsets), G, _ptr(out), M, N, K,
                                _stream_ptr(a)))
     return out
+
+
+def quantize_tg(x: torch.Tensor, q: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """bf16 [R, C] -> (E4M3 codes uint8 [R, C], fp32 per-token-group scales [R, C/32])."""
+    _need(x, "x", torch.bfloat16, 2)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, C // BLOCK), dtype=torch.float32, device=x.device)
+    _need(q, "q", E4M3_DTYPES, 2)
+    _need(scales, "scales", torch.float32, 2)
+    _same_device(x, q, scales)
+    if tuple(q.shape) != (R, C) or tuple(scales.shape) != (R, C // BLOCK):
+        raise ValueError("output shapes do not match the input")
+    _check(quantize_tg_raw(_ptr(x), R, C, _ptr(q), _ptr(scales), _stream_ptr(x)))
+    return q, scales
+
+
+def _gemm_tg_checked(raw, a, sa_rows, w, sw, out, k_major):
+    _need(a, "a", E4M3_DTYPES, 2)
+    _need(w, "b", E4M3_DTYPES, 2)
+    _need(sa_rows, "sa_rows", torch.float32, 2)
+    _need(sw, "sb", torch.float32, 2)
+    M, K = a.shape
+    if k_major:
+        N, K2 = w.shape
+        sw_shape = (N // BLOCK, K // BLOCK)
+    else:
+        K2, N = w.shape
+        sw_shape = (K // BLOCK, N // BLOCK)
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if tuple(sa_rows.shape) != (M, K // BLOCK) or tuple(sw.shape) != sw_shape:
+        raise ValueError("scale grid shapes do not match the operands")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _same_device(a, sa_rows, w, sw, out)
+    _check(raw(_ptr(a), _ptr(sa_rows), _ptr(w), _ptr(sw), _ptr(out), M, N, K, _stream_ptr(a)))
+    return out
+
+
+def gemm_tg(a: torch.Tensor, sa_rows: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+            out: torch.Tensor | None = None):
+    """E4M3 a [M, K] with per-token-group scales sa_rows [M, K/32], b [K, N], sb [K/32, N/32] -> bf16 [M, N]."""
+    return _gemm_tg_checked(gemm_tg_raw, a, sa_rows, b, sb, out, False)
+
+
+def gemm_tg_nt(a: torch.Tensor, sa_rows: torch.Tensor, bt: torch.Tensor, sbt: torch.Tensor,
+               out: torch.Tensor | None = None):
+    """As gemm_tg with the weight K-major: bt [N, K], sbt [N/32, K/32]."""
+    return _gemm_tg_checked(gemm_tg_nt_raw, a, sa_rows, bt, sbt, out, True)

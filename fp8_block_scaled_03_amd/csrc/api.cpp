@@ -55,19 +55,31 @@ const char* fp8bs_status_str(fp8bs_status s) {
   return "FP8BS: unknown status";
 }
 
-fp8bs_status fp8bs_quantize(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
-                            void* stream) {
+static fp8bs_status quantize_common(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
+                                    bool token_groups, void* stream) {
   if (rows < 0 || cols < 0) return FP8BS_EINVAL;
   if (rows > MAX_DIM || cols > MAX_DIM) return FP8BS_ESHAPE;
   if (cols % 32) return FP8BS_ESHAPE;
   if (rows == 0 || cols == 0) return FP8BS_OK;
   if (!x_bf16 || !q_e4m3 || !scales) return FP8BS_EINVAL;
   if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4)) return FP8BS_EALIGN;
+  if (token_groups)
+    return from_hip(fp8bs::launch_quantize_tg(x_bf16, rows, cols, q_e4m3, scales, (hipStream_t)stream));
   return from_hip(fp8bs::launch_quantize(x_bf16, rows, cols, q_e4m3, scales, (hipStream_t)stream));
 }
 
+fp8bs_status fp8bs_quantize(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
+                            void* stream) {
+  return quantize_common(x_bf16, rows, cols, q_e4m3, scales, false, stream);
+}
+
+fp8bs_status fp8bs_quantize_tg(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
+                               void* stream) {
+  return quantize_common(x_bf16, rows, cols, q_e4m3, scales, true, stream);
+}
+
 static fp8bs_status gemm_common(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16,
-                                int64_t M, int64_t N, int64_t K, bool k_major_b, void* stream) {
+                                int64_t M, int64_t N, int64_t K, bool k_major_b, bool act_tg, void* stream) {
   fp8bs_status st = check_gemm_dims(M, N, K);
   if (st != FP8BS_OK) return st;
   if (M == 0 || N == 0) return FP8BS_OK;
@@ -79,8 +91,8 @@ static fp8bs_status gemm_common(const void* a, const float* sa, const void* b, c
   if (st != FP8BS_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (M <= fp8bs::SMALL_M_MAX)
-    return from_hip(fp8bs::launch_gemm_smallm(a, sa, b, sb, c_bf16, M, N, K, k_major_b, s));
-  return from_hip(fp8bs::launch_gemm_tile(a, sa, b, sb, c_bf16, M, N, K, k_major_b, s));
+    return from_hip(fp8bs::launch_gemm_smallm(a, sa, b, sb, c_bf16, M, N, K, k_major_b, act_tg, s));
+  return from_hip(fp8bs::launch_gemm_tile(a, sa, b, sb, c_bf16, M, N, K, k_major_b, act_tg, s));
 }
 
 static fp8bs_status grouped_common(const void* a, const float* sa, const void* b, const float* sb,
@@ -105,12 +117,22 @@ static fp8bs_status grouped_common(const void* a, const float* sa, const void* b
 
 fp8bs_status fp8bs_gemm(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16, int64_t M,
                         int64_t N, int64_t K, void* stream) {
-  return gemm_common(a, sa, b, sb, c_bf16, M, N, K, false, stream);
+  return gemm_common(a, sa, b, sb, c_bf16, M, N, K, false, false, stream);
 }
 
 fp8bs_status fp8bs_gemm_nt(const void* a, const float* sa, const void* bt, const float* sbt, void* c_bf16,
                            int64_t M, int64_t N, int64_t K, void* stream) {
-  return gemm_common(a, sa, bt, sbt, c_bf16, M, N, K, true, stream);
+  return gemm_common(a, sa, bt, sbt, c_bf16, M, N, K, true, false, stream);
+}
+
+fp8bs_status fp8bs_gemm_tg(const void* a, const float* sa_rows, const void* b, const float* sb, void* c_bf16,
+                           int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_common(a, sa_rows, b, sb, c_bf16, M, N, K, false, true, stream);
+}
+
+fp8bs_status fp8bs_gemm_tg_nt(const void* a, const float* sa_rows, const void* bt, const float* sbt, void* c_bf16,
+                              int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_common(a, sa_rows, bt, sbt, c_bf16, M, N, K, true, true, stream);
 }
 
 fp8bs_status fp8bs_grouped_gemm(const void* a, const float* sa, const void* b, const float* sb,

@@ -31,6 +31,33 @@
 namespace fp8bs {
 
 // ------------------------------------------------------------------------------------
+// direct global->LDS loads
+// ------------------------------------------------------------------------------------
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4:
+// lane l's bytes land at M0 + 16*l; M0 = LDS byte address of the wave's 1 KB
+// destination).  Issued from inline asm so that the compiler does not drain
+// every load before the next LDS read; the callers wait with explicit vmcnt
+// counts (a wave's loads complete in issue order).  Nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
+               : "memory");
+}
+// The same with 4 bytes per lane (lane l's dword lands at M0 + 4*l).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr)
+               : "memory");
+}
+// Workgroup barrier that orders LDS only: the direct loads in flight keep
+// running (a plain __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// ------------------------------------------------------------------------------------
 // tile kernel
 // ------------------------------------------------------------------------------------
 constexpr int TBM = 256, TBN = 256, TTHREADS = 512;
@@ -42,7 +69,13 @@ constexpr int TILE_STAGES = 3;
 // K-blocks (double-buffered in LDS): per K-block 8 row-blocks x 8 column-blocks.
 constexpr int SCW = 64;
 constexpr int SC_WINDOW_BYTES = SCW * 8 * 8 * 4;  // 16 KB
-constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + 2 * SC_WINDOW_BYTES;  // 130 KB
+// Per-token-group activation scales: the window holds raw sa of the tile's 256
+// rows and raw sb of its 8 column blocks for SCWT K-blocks.
+constexpr int SCWT = 16;
+constexpr int TG_WINDOW_FLOATS = SCWT * (256 + 8);
+constexpr int TG_WINDOW_BYTES = TG_WINDOW_FLOATS * 4;  // 16.5 KB
+constexpr int TILE_SC_BYTES = 2 * (SC_WINDOW_BYTES > TG_WINDOW_BYTES ? SC_WINDOW_BYTES : TG_WINDOW_BYTES);
+constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + TILE_SC_BYTES;  // 131 KB
 
 // A tile in LDS: [256 rows][4 chunks of 8 bf16]; chunk c of row r lives at
 // position c ^ ((r >> 1) & 3).
@@ -71,7 +104,13 @@ struct TileArgs {
 // BT: the weight is K-major (B^T, [N, K]); its rows are staged and read exactly
 // like rows of A (K-contiguous, no transposed LDS reads), and its scale grid is
 // [NB, KB].
-template <bool BT>
+// TG: A carries per-token-group scales sa [M, KB] (one per row and K-block).
+// The MFMA then takes the B fragment as its first operand and the A fragment
+// as its second, so a lane's four outputs share one row of C (and one 32-column
+// block): the scale sa[row, kb] * sb[kb, cb] is one value per lane per
+// sub-tile.  Every kernel that takes token-group scales forms its partials
+// this way.
+template <bool BT, bool TG>
 __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem) {
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -203,6 +242,49 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     }
   };
 
+  // token-group scales: window [2][SCWT][256 rows + 8 col-blocks] of raw sa / sb.
+  // Row r = wm*64 + 16*ui + lo of the tile sits at [kk][wm][lo][ui], so a lane
+  // reads the sa of its four rows (lo = lane & 15, ui = 0..3) with one 16-byte
+  // read.
+  // Filled with direct global->LDS dword loads (no registers): dword d of the
+  // window is loaded by lane d % 64 of load d / 64, and waited for with an
+  // explicit vmcnt(0) before the barrier that ends the iteration.
+  const uint32_t sc_lds_addr = (uint32_t)(uintptr_t)((lds_u8*)sc_lds);
+  auto load_tg_window = [&](int win) __attribute__((always_inline)) {
+    const uint32_t dst = sc_lds_addr + (win & 1) * TG_WINDOW_BYTES;
+    for (int i = w; i < TG_WINDOW_FLOATS / 64; i += TTHREADS / 64) {
+      const int pos = i * 64 + lane;
+      const float* src;
+      if (pos < SCWT * 256) {
+        const int kk = pos >> 8, within = pos & 255;
+        const int rr = (within >> 6) * 64 + (within & 3) * 16 + ((within >> 2) & 15);
+        int kb = win * SCWT + kk;
+        kb = kb < KB ? kb : KB - 1;
+        int64_t row = p.row0 + rr;
+        row = row < p.row_end ? row : p.row_end - 1;
+        src = p.sa + row * KB + kb;
+      } else {
+        const int j = pos - SCWT * 256, kk = j >> 3, cbl = j & 7;
+        int kb = win * SCWT + kk;
+        kb = kb < KB ? kb : KB - 1;
+        int64_t cb = cb_tile + cbl;
+        cb = cb < NB ? cb : NB - 1;
+        src = BT ? p.sb + cb * KB + kb : p.sb + (int64_t)kb * NB + cb;
+      }
+      dma4(src, dst + i * 256);
+    }
+  };
+  // sa of the lane's four rows stays in VGPRs; the wave-uniform sb of its four
+  // column blocks moves to SGPRs (the tile kernel has no VGPRs to spare)
+  auto read_tg_scales = [&](int kb, v4f_t& sa4, float (&sbs)[4]) __attribute__((always_inline)) {
+    const float* w0 = sc_lds + ((kb / SCWT) & 1) * TG_WINDOW_FLOATS;
+    const int kk = kb % SCWT;
+    sa4 = *reinterpret_cast<const v4f_t*>(w0 + kk * 256 + wm * 64 + (lane & 15) * 4);
+    const v4f_t sb4 = *reinterpret_cast<const v4f_t*>(w0 + SCWT * 256 + kk * 8 + 4 * wn);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sbs[j] = uniform_f32(sb4[j]);
+  };
+
   v4f acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -213,7 +295,14 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // K-block 0's fragments in registers
   // K = 0: no operand or scale is touched (the caller may pass null pointers);
   // the accumulators stay zero.
-  if (KB > 0) load_scale_window(0);
+  if (KB > 0) {
+    if constexpr (TG) {
+      load_tg_window(0);
+      wait_vmcnt<0>();
+    } else {
+      load_scale_window(0);
+    }
+  }
   uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
   if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
   if (KB > 1) { load_stage(1, ra, rb); store_stage(1, ra, rb); }
@@ -237,10 +326,20 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // right after the last promotion, into the same registers, so the barrier
   // hides the LDS latency
   float s_cur[2][4];
-  if (KB > 0) read_scales(0, s_cur);
+  v4f_t sa4 = {0.0f, 0.0f, 0.0f, 0.0f}, s4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  float sbs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (KB > 0) {
+    if constexpr (TG) read_tg_scales(0, sa4, sbs);
+    else read_scales(0, s_cur);
+  }
   for (int kb = 0; kb < KB; ++kb) {
-    // next window of scale products: written now, first read SCW iterations later
-    if (kb % SCW == 0 && kb + SCW < KB) load_scale_window(kb / SCW + 1);
+    // next window of scales: written now, first read SCW (SCWT) iterations later
+    const bool tg_refill = TG && kb % SCWT == 0 && kb + SCWT < KB;
+    if constexpr (TG) {
+      if (tg_refill) load_tg_window(kb / SCWT + 1);
+    } else {
+      if (kb % SCW == 0 && kb + SCW < KB) load_scale_window(kb / SCW + 1);
+    }
 
     // 32 sub-tile partials, j outer, so that each B fragment is dead after its
     // four uses and is refilled with the next K-block's; partials pass through
@@ -254,11 +353,16 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       if (q >= PDEPTH) {
         const int u = q - PDEPTH;
         const int ui = u & 3, uj = u >> 2;
-        promote(acc[ui][uj], pr[u % PDEPTH], s_cur[ui >> 1][uj >> 1]);
+        if constexpr (TG) {
+          if ((u & 7) == 0) s4 = sa4 * sbs[uj >> 1];  // this column block's four row scales
+          promote(acc[ui][uj], pr[u % PDEPTH], s4[ui]);
+        } else {
+          promote(acc[ui][uj], pr[u % PDEPTH], s_cur[ui >> 1][uj >> 1]);
+        }
       }
       if (q < 32) {
         const int qi = q & 3, qj = q >> 2;
-        pr[q % PDEPTH] = mfma_partial(af[qi], bfrag[qj]);
+        pr[q % PDEPTH] = TG ? mfma_partial(bfrag[qj], af[qi]) : mfma_partial(af[qi], bfrag[qj]);
         if (qi == 3) bfrag[qj] = read_b(sn, qj);  // last use of this B fragment
         if (qj == 7) af[qi] = read_a(sn, qi);     // last use of this A fragment
       }
@@ -271,7 +375,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       }
       if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    read_scales(kb + 1 < KB ? kb + 1 : kb, s_cur);
+    if constexpr (TG) read_tg_scales(kb + 1 < KB ? kb + 1 : kb, sa4, sbs);
+    else read_scales(kb + 1 < KB ? kb + 1 : kb, s_cur);
+    // the window's direct loads have landed before the barrier publishes them
+    // (every iteration: a wait under a branch here costs the loop its registers)
+    if constexpr (TG) wait_vmcnt<0>();
     __syncthreads();
     sn = sn == 2 ? 0 : sn + 1;
     sf = sf == 2 ? 0 : sf + 1;
@@ -286,13 +394,23 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     for (int ii = 0; ii < 2; ++ii) {
       const int i = pass * 2 + ii;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (TG) {
+          // lane holds row ii*16 + (lane&15), columns j*16 + 4*(lane>>4) + 0..3
+          const int lr = ii * 16 + (lane & 15);
+          const int lc = j * 16 + 4 * (lane >> 4);
+          const uint32_t lo = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+          const uint32_t hi = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(ep + lr * 256 + lc * 2) = make_uint2(lo, hi);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = ii * 16 + 4 * (lane >> 4) + r;
-          const int lc = j * 16 + (lane & 15);
-          *reinterpret_cast<uint16_t*>(ep + lr * 256 + lc * 2) = (uint16_t)bf16_rne(acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) {
+            const int lr = ii * 16 + 4 * (lane >> 4) + r;
+            const int lc = j * 16 + (lane & 15);
+            *reinterpret_cast<uint16_t*>(ep + lr * 256 + lc * 2) = (uint16_t)bf16_rne(acc[i][j][r]);
+          }
         }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
@@ -326,7 +444,7 @@ __device__ __forceinline__ void tile_coords(int64_t id, int64_t n_tiles, int64_t
   tn = r / gm;
 }
 
-template <bool BT>
+template <bool BT, bool TG>
 __global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __restrict__ a,
                                                              const float* __restrict__ sa,
                                                              const uint8_t* __restrict__ b,
@@ -354,7 +472,7 @@ __global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __re
   p.row_end = M;
   p.col0 = tn * TBN;
   p.sa_rows = (M + 31) >> 5;
-  tile_body<BT>(p, smem);
+  tile_body<BT, TG>(p, smem);
 }
 
 // Grouped: the grid is an upper bound on the tile count, (M_total/256 + G) x
@@ -407,7 +525,7 @@ __global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* _
   p.row_end = end;
   p.col0 = tn * TBN;
   p.sa_rows = M_total >> 5;
-  tile_body<BT>(p, smem);
+  tile_body<BT, false>(p, smem);
 }
 
 // ------------------------------------------------------------------------------------
@@ -416,30 +534,6 @@ __global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* _
 constexpr int SWAVES = 8;        // waves per workgroup; also K-blocks per round
 constexpr int STHREADS = SWAVES * 64;
 constexpr int SMALL_LDS_BUDGET = 160 * 1024;
-
-// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4:
-// lane l's bytes land at M0 + 16*l; M0 = LDS byte address of the wave's 1 KB
-// destination).  Issued from inline asm so that the compiler does not drain
-// every load before the next LDS read; the callers wait with explicit vmcnt
-// counts (a wave's loads complete in issue order).  Nothing else in these
-// kernels uses M0.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
-               : "memory");
-}
-// The same with 4 bytes per lane (lane l's dword lands at M0 + 4*l).
-__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr)
-               : "memory");
-}
-// Workgroup barrier that orders LDS only: the direct loads in flight keep
-// running (a plain __syncthreads would drain them).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Small-M kernel: a workgroup owns W = 32*NCB columns of C for all M <= 64
 // rows and all of K.  K-blocks are streamed in rounds of eight: in round r,
@@ -453,17 +547,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 // global piece p ^ f(k), where f(k) = (k / (256/W)) mod (2*NCB): the sixteen
 // rows that one 32-lane phase of a transposed read touches land in sixteen
 // different 16-byte bank groups.
-template <int MT, int NCB>
+template <int MT, int NCB, bool TG = false>
 struct SmallMCfg {
   static constexpr int W = 32 * NCB;                   // columns (= bytes of a B row) per workgroup
   static constexpr int ACH = (MT + 1) / 2;             // 1 KB chunks of A rows (32 rows each)
   static constexpr int B_BYTES = 32 * W;
-  static constexpr int SC_OFF = B_BYTES + ACH * 1024;  // 256-byte scale record after B and A
-  static constexpr int SLOT = SC_OFF + 256;
+  static constexpr int SC_OFF = B_BYTES + ACH * 1024;  // scale record(s) after B and A
+  // block scales: one 256-byte record (sa of 2 row-blocks, sb); token-group
+  // scales: sa of every row (256 bytes), then sb (256 bytes)
+  static constexpr int SLOT = SC_OFF + (TG ? 512 : 256);
   static constexpr int D_FIT = SMALL_LDS_BUDGET / (SWAVES * SLOT);
   static constexpr int D = D_FIT > 6 ? 6 : D_FIT;      // ring depth in rounds
   static constexpr int LDS = SWAVES * D * SLOT;
-  static constexpr int OPS = NCB + ACH + 1;            // direct loads per K-block
+  static constexpr int OPS = NCB + ACH + (TG ? 2 : 1);  // direct loads per K-block
   static constexpr int CS = 2 * NCB;                   // 16-column sub-tiles per workgroup
   static constexpr int RG = SWAVES / CS;               // row-tile groups
   static constexpr int TPW = (MT + RG - 1) / RG;       // row tiles per wave (at most)
@@ -477,14 +573,14 @@ __device__ __forceinline__ int small_b_swz(int k) {
   return (k / (8 / NCB)) & (2 * NCB - 1);
 }
 
-template <int MT, int NCB>
+template <int MT, int NCB, bool TG>
 __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __restrict__ a,
                                                                const float* __restrict__ sa,
                                                                const uint8_t* __restrict__ b,
                                                                const float* __restrict__ sb,
                                                                uint16_t* __restrict__ c, int64_t M, int64_t N,
                                                                int64_t K) {
-  using Cfg = SmallMCfg<MT, NCB>;
+  using Cfg = SmallMCfg<MT, NCB, TG>;
   constexpr int D = Cfg::D, W = Cfg::W;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -523,6 +619,10 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
   const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
   const float* const sc_src = lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sb + cb0 + sbj;
   const int64_t sc_stride = lane < 2 ? 1 : NB;
+  // token-group scales: record 1, lane l = sa of row min(l, M-1); record 2,
+  // lane l = sb of column block cb0 + min(l, NCB-1)
+  const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
+  const float* const tg_sb_src = sb + cb0 + (lane < NCB ? lane : NCB - 1);
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   const uint32_t ring_w = (uint32_t)(uintptr_t)((lds_u8*)(smem + w * D * Cfg::SLOT));
 
@@ -534,7 +634,12 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
     for (int i = 0; i < NCB; ++i) dma16(b_src[i] + (int64_t)kc * 32 * N, sl + i * 1024);
 #pragma unroll
     for (int ch = 0; ch < Cfg::ACH; ++ch) dma16(a_src[ch] + (int64_t)kc * 32, sl + Cfg::B_BYTES + ch * 1024);
-    dma4(sc_src + kc * sc_stride, sl + Cfg::SC_OFF);
+    if constexpr (TG) {
+      dma4(tg_sa_src + kc, sl + Cfg::SC_OFF);
+      dma4(tg_sb_src + (int64_t)kc * NB, sl + Cfg::SC_OFF + 256);
+    } else {
+      dma4(sc_src + kc * sc_stride, sl + Cfg::SC_OFF);
+    }
   };
 
   // ---- ownership: 16-column sub-tile cs, row tiles rg, rg + RG, ... ----
@@ -564,7 +669,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
     constexpr bool FULL = decltype(FULL_)::value;
     v2i braw[SWAVES];
     v2i araw[SWAVES][Cfg::TPW];
-    float sbv[SWAVES], sav[SWAVES][2];
+    float sbv[SWAVES], sav[SWAVES][2], sat[SWAVES][Cfg::TPW];
 #pragma unroll
     for (int q = 0; q < SWAVES; ++q) {
       const unsigned char* sl = smem + (q * D + slot) * Cfg::SLOT;
@@ -573,17 +678,25 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
       for (int t = 0; t < Cfg::TPW; ++t)
         araw[q][t] = *reinterpret_cast<const v2i*>(sl + a_frag_off + tile_of(t) * 16 * 32);
       const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF);
-      sav[q][0] = scr[0];
-      sav[q][1] = scr[1];
-      sbv[q] = scr[2 + own_cb];
+      if constexpr (TG) {
+        // this lane's row scale in each owned row tile (rows 16*i + (lane&15))
+#pragma unroll
+        for (int t = 0; t < Cfg::TPW; ++t) sat[q][t] = scr[16 * tile_of(t) + (lane & 15)];
+        sbv[q] = scr[64 + own_cb];
+      } else {
+        sav[q][0] = scr[0];
+        sav[q][1] = scr[1];
+        sbv[q] = scr[2 + own_cb];
+      }
     }
 #pragma unroll
     for (int q = 0; q < SWAVES; ++q) {
       const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
 #pragma unroll
       for (int t = 0; t < Cfg::TPW; ++t) {
-        const v4f p = mfma_partial(e4m3x8_to_bf16x8(araw[q][t]), bfrag);
-        const float sc = sav[q][tile_of(t) >> 1] * sbv[q];
+        const v8bf afrag = e4m3x8_to_bf16x8(araw[q][t]);
+        const v4f p = TG ? mfma_partial(bfrag, afrag) : mfma_partial(afrag, bfrag);
+        const float sc = (TG ? sat[q][t] : sav[q][tile_of(t) >> 1]) * sbv[q];
         if (FULL || q < nkb) promote(acc[t], p, sc);
       }
     }
@@ -608,15 +721,26 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
   }
   wait_vmcnt<0>();  // drain the extra loads before the workgroup ends
 
-  const int col = (int)n0 + cs * 16 + (lane & 15);
 #pragma unroll
   for (int t = 0; t < Cfg::TPW; ++t) {
     const int i = rg + t * Cfg::RG;
     if (owns && i < MT) {
+      if constexpr (TG) {
+        // lane holds row 16*i + (lane&15), columns cs*16 + 4*(lane>>4) + 0..3
+        const int64_t row = i * 16 + (lane & 15);
+        const int64_t col4 = n0 + cs * 16 + 4 * (lane >> 4);
+        if (row < M) {
+          const uint32_t lo = bf16_rne(acc[t][0]) | (bf16_rne(acc[t][1]) << 16);
+          const uint32_t hi = bf16_rne(acc[t][2]) | (bf16_rne(acc[t][3]) << 16);
+          *reinterpret_cast<uint2*>(c + row * N + col4) = make_uint2(lo, hi);
+        }
+      } else {
+        const int col = (int)n0 + cs * 16 + (lane & 15);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
-        if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
+          if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+        }
       }
     }
   }
@@ -634,17 +758,18 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
 // (record q: sa of row-blocks 0 and 1, sb of the NCB column blocks, for K-block
 // 8r+q).  Every wave issues NCB 1 KB weight loads, ACH 1 KB A loads and one
 // scale record per round.
-template <int MT, int NCB>
+template <int MT, int NCB, bool TG = false>
 struct SmallMNtCfg {
   static constexpr int W = 32 * NCB;
   static constexpr int ACH = (MT + 1) / 2;
   static constexpr int A_OFF = W * 256;
   static constexpr int SC_OFF = A_OFF + 32 * ACH * 256;
-  static constexpr int SLOT = SC_OFF + SWAVES * 256;
+  static constexpr int REC = TG ? 512 : 256;  // scale record per K-block (token groups: sa rows, then sb)
+  static constexpr int SLOT = SC_OFF + SWAVES * REC;
   static constexpr int D_FIT = SMALL_LDS_BUDGET / SLOT;
   static constexpr int D = D_FIT > 6 ? 6 : D_FIT;
   static constexpr int LDS = D * SLOT;
-  static constexpr int OPS = NCB + ACH + 1;
+  static constexpr int OPS = NCB + ACH + (TG ? 2 : 1);
   static constexpr int CS = 2 * NCB;
   static constexpr int RG = SWAVES / CS;
   static constexpr int TPW = (MT + RG - 1) / RG;
@@ -653,14 +778,14 @@ struct SmallMNtCfg {
   static_assert((D - 2) * OPS < 64, "vmcnt range");
 };
 
-template <int MT, int NCB>
+template <int MT, int NCB, bool TG>
 __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t* __restrict__ a,
                                                                   const float* __restrict__ sa,
                                                                   const uint8_t* __restrict__ bt,
                                                                   const float* __restrict__ sbt,
                                                                   uint16_t* __restrict__ c, int64_t M, int64_t N,
                                                                   int64_t K) {
-  using Cfg = SmallMNtCfg<MT, NCB>;
+  using Cfg = SmallMNtCfg<MT, NCB, TG>;
   constexpr int D = Cfg::D, W = Cfg::W;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -702,6 +827,10 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
   const int nrb = (int)((M + 31) >> 5);
   const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
   const float* const sc_src = lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sbt + (int64_t)(cb0 + sbj) * KB;
+  // token-group scales: record 1, lane l = sa of row min(l, M-1); record 2,
+  // lane l = sbt of column block cb0 + min(l, NCB-1)
+  const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
+  const float* const tg_sb_src = sbt + (int64_t)(cb0 + (lane < NCB ? lane : NCB - 1)) * KB;
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
 
@@ -721,7 +850,12 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
       if (ch < a_live) dma16(a_row[ch] + koff(r, a_g[ch]), sl + Cfg::A_OFF + (w + 8 * ch) * 1024);
     int kc = r * SWAVES + w;
     kc = kc < KB ? kc : KB - 1;
-    dma4(sc_src + kc, sl + Cfg::SC_OFF + w * 256);
+    if constexpr (TG) {
+      dma4(tg_sa_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+      dma4(tg_sb_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC + 256);
+    } else {
+      dma4(sc_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+    }
   };
 
   // ---- ownership (as in the [K, N] kernel): 16-column sub-tile cs, row tiles rg, rg + RG, ...
@@ -749,25 +883,32 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
     const unsigned char* sl = smem + slot * Cfg::SLOT;
     v2i braw[SWAVES];
     v2i araw[SWAVES][Cfg::TPW];
-    float sbv[SWAVES], sav[SWAVES][2];
+    float sbv[SWAVES], sav[SWAVES][2], sat[SWAVES][Cfg::TPW];
 #pragma unroll
     for (int q = 0; q < SWAVES; ++q) {
       braw[q] = *reinterpret_cast<const v2i*>(sl + frag_off(16 * cs + (lane & 15), q));
 #pragma unroll
       for (int t = 0; t < Cfg::TPW; ++t)
         araw[q][t] = *reinterpret_cast<const v2i*>(sl + Cfg::A_OFF + frag_off(16 * tile_of(t) + (lane & 15), q));
-      const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF + q * 256);
-      sav[q][0] = scr[0];
-      sav[q][1] = scr[1];
-      sbv[q] = scr[2 + own_cb];
+      const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF + q * Cfg::REC);
+      if constexpr (TG) {
+#pragma unroll
+        for (int t = 0; t < Cfg::TPW; ++t) sat[q][t] = scr[16 * tile_of(t) + (lane & 15)];
+        sbv[q] = scr[64 + own_cb];
+      } else {
+        sav[q][0] = scr[0];
+        sav[q][1] = scr[1];
+        sbv[q] = scr[2 + own_cb];
+      }
     }
 #pragma unroll
     for (int q = 0; q < SWAVES; ++q) {
       const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
 #pragma unroll
       for (int t = 0; t < Cfg::TPW; ++t) {
-        const v4f p = mfma_partial(e4m3x8_to_bf16x8(araw[q][t]), bfrag);
-        const float sc = sav[q][tile_of(t) >> 1] * sbv[q];
+        const v8bf afrag = e4m3x8_to_bf16x8(araw[q][t]);
+        const v4f p = TG ? mfma_partial(bfrag, afrag) : mfma_partial(afrag, bfrag);
+        const float sc = (TG ? sat[q][t] : sav[q][tile_of(t) >> 1]) * sbv[q];
         if (FULL || q < nkb) promote(acc[t], p, sc);
       }
     }
@@ -781,7 +922,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
   }
   for (int r = 0; r < rounds; ++r) {
     // this wave's round-r loads have landed: NCB + a_live + 1 loads per round
-    constexpr int LB = (D - 2) * (NCB + 1);
+    constexpr int LB = (D - 2) * (NCB + (TG ? 2 : 1));
     if (a_live == 0) wait_vmcnt<LB>();
     else if (a_live == 1) wait_vmcnt<LB + (D - 2)>();
     else wait_vmcnt<LB + 2 * (D - 2)>();
@@ -795,15 +936,26 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
   wait_vmcnt<0>();
   (void)n_slices;
 
-  const int col = (int)n0 + cs * 16 + (lane & 15);
 #pragma unroll
   for (int t = 0; t < Cfg::TPW; ++t) {
     const int i = rg + t * Cfg::RG;
     if (owns && i < MT) {
+      if constexpr (TG) {
+        // lane holds row 16*i + (lane&15), columns cs*16 + 4*(lane>>4) + 0..3
+        const int64_t row = i * 16 + (lane & 15);
+        const int64_t col4 = n0 + cs * 16 + 4 * (lane >> 4);
+        if (row < M) {
+          const uint32_t lo = bf16_rne(acc[t][0]) | (bf16_rne(acc[t][1]) << 16);
+          const uint32_t hi = bf16_rne(acc[t][2]) | (bf16_rne(acc[t][3]) << 16);
+          *reinterpret_cast<uint2*>(c + row * N + col4) = make_uint2(lo, hi);
+        }
+      } else {
+        const int col = (int)n0 + cs * 16 + (lane & 15);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
-        if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
+          if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+        }
       }
     }
   }
@@ -812,17 +964,26 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
 // ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
-hipError_t launch_gemm_tile(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
-                            int64_t N, int64_t K, bool k_major_b, hipStream_t stream) {
+// act_tg: A's scales are per token group, [M, K/32], instead of [ceil(M/32), K/32].
+template <bool BT, bool TG>
+static void launch_tile_t(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
   const int64_t tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + TBN - 1) / TBN;
   const int64_t n_tiles = tiles_m * tiles_n;
   const int remap = (n_tiles % 8 == 0) ? 1 : 0;
-  if (k_major_b)
-    hipLaunchKernelGGL(gemm_tile_kernel<true>, dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
-                       (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
-  else
-    hipLaunchKernelGGL(gemm_tile_kernel<false>, dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
-                       (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
+  hipLaunchKernelGGL((gemm_tile_kernel<BT, TG>), dim3((unsigned)n_tiles), dim3(TTHREADS), TILE_LDS_BYTES, stream,
+                     (const uint8_t*)a, sa, (const uint8_t*)b, sb, (uint16_t*)c, M, N, K, tiles_m, tiles_n, remap);
+}
+
+hipError_t launch_gemm_tile(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
+                            int64_t N, int64_t K, bool k_major_b, bool act_tg, hipStream_t stream) {
+  if (k_major_b) {
+    if (act_tg) launch_tile_t<true, true>(a, sa, b, sb, c, M, N, K, stream);
+    else launch_tile_t<true, false>(a, sa, b, sb, c, M, N, K, stream);
+  } else {
+    if (act_tg) launch_tile_t<false, true>(a, sa, b, sb, c, M, N, K, stream);
+    else launch_tile_t<false, false>(a, sa, b, sb, c, M, N, K, stream);
+  }
   return hipGetLastError();
 }
 
@@ -868,80 +1029,88 @@ int smallm_nt_ncb(int64_t N) {
   return best;
 }
 
-template <int MT, int NCB, bool NT>
+template <int MT, int NCB, bool NT, bool TG>
 static void launch_smallm_t(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if constexpr (NT) {
-    using Cfg = SmallMNtCfg<MT, NCB>;
-    hipLaunchKernelGGL((gemm_smallm_nt_kernel<MT, NCB>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
+    using Cfg = SmallMNtCfg<MT, NCB, TG>;
+    hipLaunchKernelGGL((gemm_smallm_nt_kernel<MT, NCB, TG>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
                        stream, a, sa, b, sb, c, M, N, K);
   } else {
-    using Cfg = SmallMCfg<MT, NCB>;
-    hipLaunchKernelGGL((gemm_smallm_kernel<MT, NCB>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
+    using Cfg = SmallMCfg<MT, NCB, TG>;
+    hipLaunchKernelGGL((gemm_smallm_kernel<MT, NCB, TG>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
                        stream, a, sa, b, sb, c, M, N, K);
   }
 }
 
-template <int NCB, bool NT>
+template <int NCB, bool NT, bool TG>
 static void launch_smallm_n(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   switch ((int)((M + 15) / 16)) {
-    case 1: launch_smallm_t<1, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
-    case 2: launch_smallm_t<2, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
-    case 3: launch_smallm_t<3, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
-    default: launch_smallm_t<4, NCB, NT>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 1: launch_smallm_t<1, NCB, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 2: launch_smallm_t<2, NCB, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 3: launch_smallm_t<3, NCB, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
+    default: launch_smallm_t<4, NCB, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
+  }
+}
+
+template <bool NT, bool TG>
+static void launch_smallm_l(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  switch (NT ? smallm_nt_ncb(N) : smallm_ncb(N)) {
+    case 4: launch_smallm_n<4, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
+    case 2: launch_smallm_n<2, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
+    default: launch_smallm_n<1, NT, TG>(a, sa, b, sb, c, M, N, K, stream); break;
   }
 }
 
 hipError_t launch_gemm_smallm(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
-                              int64_t N, int64_t K, bool k_major_b, hipStream_t stream) {
+                              int64_t N, int64_t K, bool k_major_b, bool act_tg, hipStream_t stream) {
   const uint8_t* a8 = (const uint8_t*)a;
   const uint8_t* b8 = (const uint8_t*)b;
   uint16_t* c16 = (uint16_t*)c;
   if (k_major_b) {
-    switch (smallm_nt_ncb(N)) {
-      case 4: launch_smallm_n<4, true>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-      case 2: launch_smallm_n<2, true>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-      default: launch_smallm_n<1, true>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-    }
+    if (act_tg) launch_smallm_l<true, true>(a8, sa, b8, sb, c16, M, N, K, stream);
+    else launch_smallm_l<true, false>(a8, sa, b8, sb, c16, M, N, K, stream);
   } else {
-    switch (smallm_ncb(N)) {
-      case 4: launch_smallm_n<4, false>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-      case 2: launch_smallm_n<2, false>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-      default: launch_smallm_n<1, false>(a8, sa, b8, sb, c16, M, N, K, stream); break;
-    }
+    if (act_tg) launch_smallm_l<false, true>(a8, sa, b8, sb, c16, M, N, K, stream);
+    else launch_smallm_l<false, false>(a8, sa, b8, sb, c16, M, N, K, stream);
   }
   return hipGetLastError();
 }
 
-template <int MT, int NCB>
+template <int MT, int NCB, bool TG>
 static hipError_t set_smallm_attr() {
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_smallm_kernel<MT, NCB>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, SmallMCfg<MT, NCB>::LDS);
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_smallm_kernel<MT, NCB, TG>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, SmallMCfg<MT, NCB, TG>::LDS);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemm_smallm_nt_kernel<MT, NCB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             SmallMNtCfg<MT, NCB>::LDS);
+  return hipFuncSetAttribute((const void*)gemm_smallm_nt_kernel<MT, NCB, TG>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, SmallMNtCfg<MT, NCB, TG>::LDS);
 }
 
-template <int NCB>
+template <int NCB, bool TG>
 static hipError_t set_smallm_attrs() {
   hipError_t e;
-  if ((e = set_smallm_attr<1, NCB>()) != hipSuccess) return e;
-  if ((e = set_smallm_attr<2, NCB>()) != hipSuccess) return e;
-  if ((e = set_smallm_attr<3, NCB>()) != hipSuccess) return e;
-  return set_smallm_attr<4, NCB>();
+  if ((e = set_smallm_attr<1, NCB, TG>()) != hipSuccess) return e;
+  if ((e = set_smallm_attr<2, NCB, TG>()) != hipSuccess) return e;
+  if ((e = set_smallm_attr<3, NCB, TG>()) != hipSuccess) return e;
+  return set_smallm_attr<4, NCB, TG>();
 }
 
 hipError_t set_gemm_attributes() {
-  const void* tiles[4] = {(const void*)gemm_tile_kernel<false>, (const void*)gemm_tile_kernel<true>,
-                          (const void*)gemm_grouped_kernel<false>, (const void*)gemm_grouped_kernel<true>};
+  const void* tiles[6] = {(const void*)gemm_tile_kernel<false, false>, (const void*)gemm_tile_kernel<true, false>,
+                          (const void*)gemm_tile_kernel<false, true>,  (const void*)gemm_tile_kernel<true, true>,
+                          (const void*)gemm_grouped_kernel<false>,     (const void*)gemm_grouped_kernel<true>};
   hipError_t e;
   for (const void* f : tiles)
     if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, TILE_LDS_BYTES)) != hipSuccess)
       return e;
-  if ((e = set_smallm_attrs<1>()) != hipSuccess) return e;
-  if ((e = set_smallm_attrs<2>()) != hipSuccess) return e;
-  return set_smallm_attrs<4>();
+  if ((e = set_smallm_attrs<1, false>()) != hipSuccess) return e;
+  if ((e = set_smallm_attrs<2, false>()) != hipSuccess) return e;
+  if ((e = set_smallm_attrs<4, false>()) != hipSuccess) return e;
+  if ((e = set_smallm_attrs<1, true>()) != hipSuccess) return e;
+  if ((e = set_smallm_attrs<2, true>()) != hipSuccess) return e;
+  return set_smallm_attrs<4, true>();
 }
 
 }  // namespace fp8bs

@@ -5,12 +5,16 @@
 
 namespace fp8bs {
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, void* q, float* scales, hipStream_t stream);
+// per-token groups (1 x 32): scales [rows, cols/32]
+hipError_t launch_quantize_tg(const void* x, int64_t rows, int64_t cols, void* q, float* scales,
+                              hipStream_t stream);
 // k_major_b: the weight is B^T [N, K] with scales [N/32, K/32] instead of
 // B [K, N] with scales [K/32, N/32] (for grouped calls, per group).
+// act_tg: A's scales are per token group, [M, K/32] (one per row and K-block).
 hipError_t launch_gemm_tile(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
-                            int64_t N, int64_t K, bool k_major_b, hipStream_t stream);
+                            int64_t N, int64_t K, bool k_major_b, bool act_tg, hipStream_t stream);
 hipError_t launch_gemm_smallm(const void* a, const float* sa, const void* b, const float* sb, void* c, int64_t M,
-                              int64_t N, int64_t K, bool k_major_b, hipStream_t stream);
+                              int64_t N, int64_t K, bool k_major_b, bool act_tg, hipStream_t stream);
 hipError_t launch_gemm_grouped(const void* a, const float* sa, const void* b, const float* sb,
                                const int32_t* offsets, int G, void* c, int64_t M_total, int64_t N, int64_t K,
                                bool k_major_b, hipStream_t stream);

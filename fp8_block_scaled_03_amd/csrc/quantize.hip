@@ -121,6 +121,94 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint16_t* __restric
   }
 }
 
+// Per-token groups (1 row x 32 columns): the same region mapping, but each of
+// a lane's 8 rows is a quarter of its own group (the 8 columns cpart*8.. of
+// row 4k + rsub), so a group's amax is a max over the 4 lanes that differ in
+// lane bits 0 and 1, and every (row, group) gets its own scale and reciprocal.
+// The quotient and the E4M3 rounding are the block quantizer's.
+__global__ void __launch_bounds__(256) quantize_tg_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                          int64_t cols, uint8_t* __restrict__ q,
+                                                          float* __restrict__ scales, int64_t n_regions) {
+  const int lane = threadIdx.x & 63;
+  const int piece = lane & 15, rsub = lane >> 4;
+  const int b = piece >> 2, cpart = piece & 3;
+  const int64_t cb_count = cols >> 5;
+  const int64_t rg_per_row = (cb_count + Q_BLOCKS - 1) / Q_BLOCKS;
+  const int64_t waves_total = (int64_t)gridDim.x * 4;
+  for (int64_t reg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); reg < n_regions; reg += waves_total) {
+    const int64_t rb = reg / rg_per_row, g = reg - rb * rg_per_row;
+    const int64_t cb = g * Q_BLOCKS + b;
+    const bool cb_ok = cb < cb_count;
+    const int64_t col = (cb_ok ? cb : cb_count - 1) * 32 + cpart * 8;  // stays inside x
+    uint4 w[8];
+    bool ok[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t row = rb * 32 + 4 * k + rsub;
+      ok[k] = cb_ok && row < rows;
+      const int64_t rc = row < rows ? row : rows - 1;
+      w[k] = ok[k] ? *reinterpret_cast<const uint4*>(x + rc * cols + col) : make_uint4(0, 0, 0, 0);
+    }
+    float sk[8], rk[8];
+    bool all_recip = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[i])), fabsf(bf16_hi(ws[i]))));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      sk[k] = m / 448.0f;
+      const bool recip = m >= 0x1p-60f;
+      rk[k] = recip ? 1.0f / sk[k] : 0.0f;
+      all_recip = all_recip && recip;
+    }
+    auto quotient = [&](float xv, int k, auto FAST_) __attribute__((always_inline)) -> float {
+      if (decltype(FAST_)::value || rk[k] != 0.0f) {
+        const float q0 = xv * rk[k];
+        const float e = __builtin_fmaf(-q0, sk[k], xv);
+        return __builtin_copysignf(__builtin_fmaf(e, rk[k], q0), xv);
+      }
+      return sk[k] != 0.0f ? xv / sk[k] : 0.0f;
+    };
+    auto encode_store = [&](auto FAST_) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        uint32_t packed[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float t0 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i]), k, FAST_), -448.0f), 448.0f);
+          const float t1 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i]), k, FAST_), -448.0f), 448.0f);
+          const float t2 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i + 1]), k, FAST_), -448.0f), 448.0f);
+          const float t3 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i + 1]), k, FAST_), -448.0f), 448.0f);
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, wd, true);
+          packed[i] = (uint32_t)wd;
+        }
+        if (ok[k]) {
+          const int64_t row = rb * 32 + 4 * k + rsub;
+          *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
+          if (cpart == 0) scales[row * cb_count + cb] = sk[k];
+        }
+      }
+    };
+    if (__all(all_recip)) encode_store(std::true_type{});
+    else encode_store(std::false_type{});
+  }
+}
+
+hipError_t launch_quantize_tg(const void* x, int64_t rows, int64_t cols, void* q, float* scales,
+                              hipStream_t stream) {
+  const int64_t n_regions = ((rows + 31) / 32) * ((cols / 32 + Q_BLOCKS - 1) / Q_BLOCKS);
+  int64_t grid = (n_regions + 3) / 4;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(quantize_tg_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)x, rows, cols,
+                     (uint8_t*)q, scales, n_regions);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void* x, int64_t rows, int64_t cols, void* q, float* scales, hipStream_t stream) {
   const int64_t n_regions = ((rows + 31) / 32) * ((cols / 32 + Q_BLOCKS - 1) / Q_BLOCKS);
   int64_t grid = (n_regions + 3) / 4;

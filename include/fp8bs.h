@@ -128,6 +128,42 @@ fp8bs_status fp8bs_grouped_gemm_nt(const void* a, const float* sa, const void* b
                                    const int32_t* offsets_dev, int32_t G, void* c_bf16, int64_t M_total, int64_t N,
                                    int64_t K, void* stream);
 
+/*
+ * Per-token-group activation scales (one scale per row and 32 columns), the
+ * activation-side granularity that the determinism article's RMSNorm part
+ * (三, section 2, the vLLM table: per-token-group FP8 quantization fused with
+ * the norm) lists; with it an element of C depends on its own row of the
+ * bf16 activations only, so the quantize + GEMM chain is batch invariant end
+ * to end [DET part 一, sections 6-7].  Weights keep 32x32 block scales.
+ *
+ * fp8bs_quantize_tg - as fp8bs_quantize, with groups of 1 row x 32 columns:
+ *   group (r, cb) covers row r, columns [32cb, 32cb+32); amax, s = amax/448,
+ *   codes exactly as fp8bs_quantize per group [DG 2.1, 5.2].
+ *   x [rows, cols] bf16, q [rows, cols] E4M3 out, scales [rows, cols/32] fp32 out.
+ *   Checks and errors as fp8bs_quantize.
+ */
+fp8bs_status fp8bs_quantize_tg(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
+                               void* stream);
+
+/*
+ * fp8bs_gemm_tg / fp8bs_gemm_tg_nt - fp8bs_gemm / fp8bs_gemm_nt with A's
+ *   scales per token group:
+ *     C[i,j] = sum_kb  sa_rows[i, kb] * sb[kb, j/32] * sum_{k in kb} A[i,k] B[k,j]
+ *   Each 32-deep partial is formed exactly, multiplied by the fp32 product
+ *   sa_rows[i,kb]*sb (one rounding) and added into one fp32 accumulator, K-blocks
+ *   ascending; C is rounded once to bf16.  Every kernel behind these two
+ *   entry points forms its partials the same way, so results do not depend on
+ *   M or on the kernel.
+ *   a [M, K] E4M3, sa_rows [M, K/32] fp32 (4-byte aligned);
+ *   fp8bs_gemm_tg:    b  [K, N] E4M3, sb  [K/32, N/32] fp32
+ *   fp8bs_gemm_tg_nt: bt [N, K] E4M3, sbt [N/32, K/32] fp32
+ *   c [M, N] bf16 out.  Checks, errors and K == 0 as for fp8bs_gemm.
+ */
+fp8bs_status fp8bs_gemm_tg(const void* a, const float* sa_rows, const void* b, const float* sb, void* c_bf16,
+                           int64_t M, int64_t N, int64_t K, void* stream);
+fp8bs_status fp8bs_gemm_tg_nt(const void* a, const float* sa_rows, const void* bt, const float* sbt, void* c_bf16,
+                              int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8bs_status_str(fp8bs_status status);
 

@@ -23,8 +23,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = _declared_functions()
-    assert names == ["fp8bs_gemm", "fp8bs_gemm_nt", "fp8bs_grouped_gemm", "fp8bs_grouped_gemm_nt", "fp8bs_quantize",
-                     "fp8bs_status_str"]
+    assert names == ["fp8bs_gemm", "fp8bs_gemm_nt", "fp8bs_gemm_tg", "fp8bs_gemm_tg_nt", "fp8bs_grouped_gemm",
+                     "fp8bs_grouped_gemm_nt", "fp8bs_quantize", "fp8bs_quantize_tg", "fp8bs_status_str"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -37,8 +37,8 @@ def test_status_strings():
     assert lib.fp8bs_status_str(99).decode()
 
 
-def test_quantize_argument_checks():
-    q = binding.quantize_raw
+@pytest.mark.parametrize("q", [binding.quantize_raw, binding.quantize_tg_raw])
+def test_quantize_argument_checks(q):
     assert q(A16, 0, 64, A16, A4) == OK            # empty: no-op
     assert q(A16, 5, 0, A16, A4) == OK
     assert q(A16, -1, 64, A16, A4) == EINVAL
@@ -70,8 +70,8 @@ def test_gemm_argument_checks():
     assert g(A16, A4, A16, A4, A16, 4, 64, (1 << 30) + 32) == ESHAPE
 
 
-@pytest.mark.parametrize("g", [binding.gemm_raw, binding.gemm_nt_raw])
-def test_gemm_argument_checks_both_layouts(g):
+@pytest.mark.parametrize("g", [binding.gemm_raw, binding.gemm_nt_raw, binding.gemm_tg_raw, binding.gemm_tg_nt_raw])
+def test_gemm_argument_checks_all_variants(g):
     assert g(A16, A4, A16, A4, A16, 0, 64, 64) == OK
     assert g(A16, A4, A16, A4, A16, 4, 64, 48) == ESHAPE
     assert g(A16, A4, A16, A4, A16, 4, 40, 64) == ESHAPE
