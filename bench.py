@@ -13,6 +13,8 @@ Also measured (same run, reported under "detail"):
   * the small-M (decode) GEMM at K=8192, M in {1, 8, 32, 64}, N in
     {8192, 28672}: algorithmic HBM bytes per launch over the kernel time;
   * the quantizer alone (HBM bytes per launch over its time);
+  * the same for per-token-group (1 x 32) activation scales: quantizer, square
+    GEMM and the decode sweep in both weight layouts;
   * the CPU oracle on a bounded sample of the same workload ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
@@ -185,51 +187,59 @@ def main():
     }
 
     if not args.quick:
-        decode = []
-        for n_dec in (8192, 28672):
-            dwl = W.decode(64, n_dec)
-            a64 = to_dev_bf16(dwl.a_bits())
-            db = to_dev_bf16(dwl.b_bits())
-            q64, s64 = fp8bs.quantize(a64)
-            dqb, dsb = fp8bs.quantize(db)
-            for m in (1, 8, 32, 64):
-                dqa, dsa = q64[:m].contiguous(), s64[:(m + 31) // 32].contiguous()
-                dc = torch.empty((m, n_dec), dtype=torch.bfloat16, device=dev)
-                fn = (lambda dqa=dqa, dsa=dsa, dc=dc: fp8bs.gemm(dqa, dsa, dqb, dsb, out=dc))
-                for _ in range(3):
-                    fn()
-                d_med, d_min, d_avg = time_launch(fn, reps)
-                nbytes = m * dwl.K + dwl.K * n_dec + 4 * ((m + 31) // 32) * (dwl.K // 32) \
-                    + 4 * (dwl.K // 32) * (n_dec // 32) + 2 * m * n_dec
-                decode.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
-                               "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
-                               "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-            del a64, db, q64, s64, dqb, dsb
-        detail["decode_small_m"] = decode
+        def decode_sweep(k_major, token_groups):
+            """K = 8192, M in {1, 8, 32, 64} (prefixes of one 64-row A), both N:
+            algorithmic bytes (codes, both scale grids, C) over the kernel time."""
+            gemm = {(False, False): fp8bs.gemm, (True, False): fp8bs.gemm_nt,
+                    (False, True): fp8bs.gemm_tg, (True, True): fp8bs.gemm_tg_nt}[(k_major, token_groups)]
+            quant_a = fp8bs.quantize_tg if token_groups else fp8bs.quantize
+            rows_out = []
+            for n_dec in (8192, 28672):
+                dwl = W.decode(64, n_dec)
+                KB = dwl.K // 32
+                w_bits = dwl.b_bits()
+                if k_major:
+                    w_bits = np.ascontiguousarray(w_bits.T)
+                q64, s64 = quant_a(to_dev_bf16(dwl.a_bits()))
+                dqw, dsw = fp8bs.quantize(to_dev_bf16(w_bits))
+                del w_bits
+                for m in (1, 8, 32, 64):
+                    sa_rows = m if token_groups else (m + 31) // 32
+                    dqa, dsa = q64[:m].contiguous(), s64[:sa_rows].contiguous()
+                    dc = torch.empty((m, n_dec), dtype=torch.bfloat16, device=dev)
+                    fn = (lambda dqa=dqa, dsa=dsa, dc=dc: gemm(dqa, dsa, dqw, dsw, out=dc))
+                    for _ in range(3):
+                        fn()
+                    d_med, d_min, d_avg = time_launch(fn, reps)
+                    nbytes = m * dwl.K + dwl.K * n_dec + 4 * sa_rows * KB + 4 * KB * (n_dec // 32) + 2 * m * n_dec
+                    rows_out.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
+                                     "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
+                                     "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                del q64, s64, dqw, dsw
+            return rows_out
 
-        # the same sweep with the weight K-major (B^T [N, K], the layout of the
-        # pages' call interface): each workgroup streams whole weight rows
-        decode_nt = []
-        for n_dec in (8192, 28672):
-            dwl = W.decode(64, n_dec)
-            a64 = to_dev_bf16(dwl.a_bits())
-            dbt = to_dev_bf16(np.ascontiguousarray(dwl.b_bits().T))
-            q64, s64 = fp8bs.quantize(a64)
-            dqbt, dsbt = fp8bs.quantize(dbt)
-            for m in (1, 8, 32, 64):
-                dqa, dsa = q64[:m].contiguous(), s64[:(m + 31) // 32].contiguous()
-                dc = torch.empty((m, n_dec), dtype=torch.bfloat16, device=dev)
-                fn = (lambda dqa=dqa, dsa=dsa, dc=dc: fp8bs.gemm_nt(dqa, dsa, dqbt, dsbt, out=dc))
-                for _ in range(3):
-                    fn()
-                d_med, d_min, d_avg = time_launch(fn, reps)
-                nbytes = m * dwl.K + dwl.K * n_dec + 4 * ((m + 31) // 32) * (dwl.K // 32) \
-                    + 4 * (dwl.K // 32) * (n_dec // 32) + 2 * m * n_dec
-                decode_nt.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
-                                  "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
-                                  "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-            del a64, dbt, q64, s64, dqbt, dsbt
-        detail["decode_small_m_k_major_weight"] = decode_nt
+        detail["decode_small_m"] = decode_sweep(False, False)
+        # the weight K-major (B^T [N, K], the layout of the pages' call
+        # interface): each workgroup streams whole weight rows
+        detail["decode_small_m_k_major_weight"] = decode_sweep(True, False)
+
+        # per-token-group activation scales (1 x 32): quantizer, square GEMM, decode
+        sa_tg = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
+        fp8bs.quantize_tg(a, qa, sa_tg)
+        tq_med, _, _ = time_launch(lambda: fp8bs.quantize_tg(a, qa, sa_tg), reps)
+        tg_fn = lambda: fp8bs.gemm_tg(qa, sa_tg, qb, sb, out=c)
+        for _ in range(3):
+            tg_fn()
+        tg_med, _, tg_avg = time_launch(tg_fn, reps)
+        detail["token_groups"] = {
+            "quantize_tg_4096x4096_ms_median": round(tq_med, 5),
+            "quantize_tg_4096x4096_gbs": round((2 * M * K + M * K + 4 * M * (K // 32)) / (tq_med * 1e-3) / 1e9, 1),
+            "gemm_tg_4096_ms_median": round(tg_med, 5),
+            "gemm_tg_4096_tflops_median": round(gemm_flops / (tg_med * 1e-3) / 1e12, 1),
+            "decode_k_major_weight": decode_sweep(True, True),
+            "decode": decode_sweep(False, True),
+        }
+        del sa_tg
 
         # prefill M = K = 8192, N = 28672 and the grouped workload (GEMM only)
         pwl = W.prefill(28672)
