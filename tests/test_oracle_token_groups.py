@@ -72,3 +72,17 @@ def test_token_group_gemm_matches_exact_rational_per_row(M, N, K):
         ex = np.vectorize(float)(gemm_exact(qa[i:i + 1], sa[i:i + 1], qb, sb))[0]
         assert np.all(np.abs(ref[i] - ex) <= gam * absref[i] + 1e-300), i
         assert np.all(np.abs(ref_nt[i] - ex) <= gam * absref[i] + 1e-300), i
+
+
+def test_token_group_gemm_with_block_scales_repeated_is_block_gemm():
+    """Token-group scales that repeat a 32x32 grid's scale on each of its rows
+    describe the same dequantized A, so the two references agree exactly."""
+    from oracle import gemm_ref
+    g = np.random.default_rng(9)
+    M, N, K = 70, 64, 96
+    qa, qb = _rand_codes(g, (M, K)), _rand_codes(g, (K, N))
+    sa, sb = _rand_scales(g, (3, K // 32)), _rand_scales(g, (K // 32, N // 32))
+    sa_rows = np.repeat(sa, 32, axis=0)[:M]
+    ref_tg, abs_tg = gemm_ref_tg(qa, sa_rows, qb, sb)
+    ref, absref = gemm_ref(qa, sa, qb, sb)
+    assert np.array_equal(ref_tg, ref) and np.array_equal(abs_tg, absref)
