@@ -15,7 +15,9 @@ cites the passage of the source pages it follows:
   (call interface).
 * "Determinism article" = "AI Infra 进阶：如何让大模型输出确定的结果"
   (aif.amtbbs.org, post 29992): introduction (FP16 encoding table and the
-  round-half-to-even example) and part 一 (GEMM batch invariance).
+  round-half-to-even example), part 一 (GEMM batch invariance) and part 三
+  (RMSNorm, its residual-add form and the per-token-group quantizer fused
+  with it).
 * "Triton-cutlass article" = "Triton内核命名嵌入Cutlass：自动调用FP8 Tensor
   Core GEMM路径..." (blog.hotdry.top, 2025-10-04): the tiled GEMM listing in the
   section on deployable parameters (a plain GEMM with fp32 accumulation).
@@ -31,6 +33,7 @@ from .gemm import (dequantize, dequantize_token_groups, gemm_ref, gemm_ref_at, g
                    gemm_ref_tg_nt, grouped_gemm_ref, grouped_gemm_ref_at, grouped_gemm_ref_nt, tolerance_ok,
                    tolerance_bound, bf16_bits_to_f64)
 from .exact import gemm_exact
+from .rmsnorm import residual_add, rmsnorm_ref, rmsnorm_tolerance_ok, RMS_REL_TOL, RMS_ABS_TOL
 
 __all__ = [
     "Minifloat", "E4M3FN", "FP16", "BF16",
@@ -41,4 +44,5 @@ __all__ = [
     "grouped_gemm_ref_nt",
     "tolerance_ok", "tolerance_bound", "bf16_bits_to_f64",
     "gemm_exact",
+    "residual_add", "rmsnorm_ref", "rmsnorm_tolerance_ok", "RMS_REL_TOL", "RMS_ABS_TOL",
 ]
