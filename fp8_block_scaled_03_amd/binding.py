@@ -59,6 +59,8 @@ def load_library() -> ctypes.CDLL:
         lib.fp8bs_gemm_tg_nt.restype = ctypes.c_int
         lib.fp8bs_grouped_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, i64, i64, vp]
         lib.fp8bs_grouped_gemm_nt.restype = ctypes.c_int
+        lib.fp8bs_rmsnorm_quantize_tg.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp]
+        lib.fp8bs_rmsnorm_quantize_tg.restype = ctypes.c_int
         lib.fp8bs_status_str.argtypes = [ctypes.c_int]
         lib.fp8bs_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -118,6 +120,11 @@ def gemm_tg_raw(a_ptr, sa_ptr, b_ptr, sb_ptr, c_ptr, M, N, K, stream=None) -> in
 
 def gemm_tg_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) -> int:
     return load_library().fp8bs_gemm_tg_nt(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream)
+
+
+def rmsnorm_quantize_tg_raw(x_ptr, res_ptr, gamma_ptr, eps, rows, d, q_ptr, s_ptr, y_ptr, stream=None) -> int:
+    return load_library().fp8bs_rmsnorm_quantize_tg(x_ptr, res_ptr, gamma_ptr, eps, rows, d, q_ptr, s_ptr, y_ptr,
+                                                    stream)
 
 
 def gemm_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) -> int:
@@ -299,3 +306,40 @@ def gemm_tg_nt(a: torch.Tensor, sa_rows: torch.Tensor, bt: torch.Tensor, sbt: to
                out: torch.Tensor | None = None):
     """As gemm_tg with the weight K-major: bt [N, K], sbt [N/32, K/32]."""
     return _gemm_tg_checked(gemm_tg_nt_raw, a, sa_rows, bt, sbt, out, True)
+
+
+def rmsnorm_quantize_tg(x: torch.Tensor, gamma: torch.Tensor, eps: float, residual: torch.Tensor | None = None,
+                        q: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                        y: torch.Tensor | None = None, want_y: bool = False):
+    """Residual add (in place on ``residual`` when given) + RMSNorm + per-token-group
+    quantization of bf16 x [R, d] with weight gamma [d].
+
+    Returns (q uint8 [R, d], scales fp32 [R, d/32]), plus the bf16 normalised rows
+    [R, d] as a third element when ``want_y`` is true or ``y`` is given."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(gamma, "gamma", torch.bfloat16, 1)
+    R, d = x.shape
+    if gamma.shape[0] != d:
+        raise ValueError(f"gamma has {gamma.shape[0]} entries, rows have {d}")
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, 2)
+        if tuple(residual.shape) != (R, d):
+            raise ValueError("residual has the wrong shape")
+    if q is None:
+        q = torch.empty((R, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, d // BLOCK), dtype=torch.float32, device=x.device)
+    if y is None and want_y:
+        y = torch.empty((R, d), dtype=torch.bfloat16, device=x.device)
+    _need(q, "q", E4M3_DTYPES, 2)
+    _need(scales, "scales", torch.float32, 2)
+    if tuple(q.shape) != (R, d) or tuple(scales.shape) != (R, d // BLOCK):
+        raise ValueError("output shapes do not match the input")
+    if y is not None:
+        _need(y, "y", torch.bfloat16, 2)
+        if tuple(y.shape) != (R, d):
+            raise ValueError("y has the wrong shape")
+    _same_device(*[t for t in (x, gamma, residual, q, scales, y) if t is not None])
+    _check(rmsnorm_quantize_tg_raw(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), R, d, _ptr(q), _ptr(scales),
+                                   _ptr(y), _stream_ptr(x)))
+    return (q, scales) if y is None else (q, scales, y)

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 
 #include "launch.hpp"
@@ -76,6 +77,21 @@ fp8bs_status fp8bs_quantize(const void* x_bf16, int64_t rows, int64_t cols, void
 fp8bs_status fp8bs_quantize_tg(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, float* scales,
                                void* stream) {
   return quantize_common(x_bf16, rows, cols, q_e4m3, scales, true, stream);
+}
+
+fp8bs_status fp8bs_rmsnorm_quantize_tg(const void* x_bf16, void* residual_bf16, const void* gamma_bf16, float eps,
+                                       int64_t rows, int64_t d, void* q_e4m3, float* scales, void* y_bf16,
+                                       void* stream) {
+  if (rows < 0 || d < 0) return FP8BS_EINVAL;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return FP8BS_EINVAL;
+  if (rows > MAX_DIM || d % 32 || d > fp8bs::rmsnorm_max_cols()) return FP8BS_ESHAPE;
+  if (rows == 0 || d == 0) return FP8BS_OK;
+  if (!x_bf16 || !gamma_bf16 || !q_e4m3 || !scales) return FP8BS_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(gamma_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4) ||
+      (residual_bf16 && !aligned(residual_bf16, 16)) || (y_bf16 && !aligned(y_bf16, 16)))
+    return FP8BS_EALIGN;
+  return from_hip(fp8bs::launch_rmsnorm_quantize_tg(x_bf16, residual_bf16, gamma_bf16, eps, rows, d, q_e4m3, scales,
+                                                    y_bf16, (hipStream_t)stream));
 }
 
 static fp8bs_status gemm_common(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16,

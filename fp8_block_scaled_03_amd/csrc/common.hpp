@@ -74,6 +74,33 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
+// ---- E4M3 quantizer steps shared by every kernel that writes codes --------------------
+// Groups with amax at or above this value take the reciprocal path below.
+constexpr float QUANT_RECIP_MIN_AMAX = 0x1p-60f;
+
+// RN32(x / s) from r = RN32(1 / s): q0 = RN(x*r), e = x - s*q0 (exact), then
+// RN(q0 + e*r) (Markstein, IBM J. Res. Dev. 34(1), 1990).  Valid when the
+// group's amax >= QUANT_RECIP_MIN_AMAX (smaller |x| of such a group give
+// quotients below 2^-33, a zero code whatever their last bits).  The sign is
+// copied from x so that -0 stays -0.
+__device__ __forceinline__ float quant_quotient_recip(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+// The same by IEEE division, for groups with a tiny amax; s = 0 gives 0.
+__device__ __forceinline__ float quant_quotient_div(float x, float s) { return s != 0.0f ? x / s : 0.0f; }
+__device__ __forceinline__ float sat448(float t) { return fminf(fmaxf(t, -448.0f), 448.0f); }
+// Four quotients (already within +-448) -> four E4M3FN bytes, round to nearest even.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float t0, float t1, float t2, float t3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
 // A value known to be equal in every lane, moved to a scalar register.
 __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));

@@ -19,6 +19,11 @@ hipError_t launch_gemm_grouped(const void* a, const float* sa, const void* b, co
                                const int32_t* offsets, int G, void* c, int64_t M_total, int64_t N, int64_t K,
                                bool k_major_b, hipStream_t stream);
 hipError_t set_gemm_attributes();
+// residual add (residual may be null) + RMSNorm + per-token-group quantizer;
+// y (the bf16 normalised rows) may be null.  d <= rmsnorm_max_cols().
+hipError_t launch_rmsnorm_quantize_tg(const void* x, void* residual, const void* gamma, float eps, int64_t rows,
+                                      int64_t d, void* q, float* scales, void* y, hipStream_t stream);
+int rmsnorm_max_cols();
 
 // M at or below which the bandwidth-oriented small-M kernel runs.  Both kernels
 // follow the same per-element recipe, so the switch never changes a result.

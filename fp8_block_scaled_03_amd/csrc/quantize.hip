@@ -36,9 +36,6 @@ __device__ __forceinline__ float block_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
 constexpr int Q_BLOCKS = 4;  // 32x32 blocks per wave region (32 rows x 128 columns)
 
 // One wave per region of 32 rows x 128 columns (256 bytes of bf16 per row).
@@ -82,15 +79,11 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint16_t* __restric
     }
     const float amax = block_max(m);
     const float s = amax / 448.0f;
-    const bool recip = amax >= 0x1p-60f;  // wave-uniform per block
+    const bool recip = amax >= QUANT_RECIP_MIN_AMAX;  // wave-uniform per block
     const float r = recip ? 1.0f / s : 0.0f;
     auto quotient = [&](float xv, auto FAST_) __attribute__((always_inline)) -> float {
-      if (decltype(FAST_)::value || recip) {
-        const float q0 = xv * r;
-        const float e = __builtin_fmaf(-q0, s, xv);
-        return __builtin_copysignf(__builtin_fmaf(e, r, q0), xv);
-      }
-      return s != 0.0f ? xv / s : 0.0f;
+      if (decltype(FAST_)::value || recip) return quant_quotient_recip(xv, s, r);
+      return quant_quotient_div(xv, s);
     };
     auto encode_store = [&](auto FAST_) __attribute__((always_inline)) {
 #pragma unroll
@@ -98,15 +91,11 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint16_t* __restric
         const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
         uint32_t packed[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const float t0 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i]), FAST_), -448.0f), 448.0f);
-          const float t1 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i]), FAST_), -448.0f), 448.0f);
-          const float t2 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i + 1]), FAST_), -448.0f), 448.0f);
-          const float t3 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i + 1]), FAST_), -448.0f), 448.0f);
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, wd, true);
-          packed[i] = (uint32_t)wd;
-        }
+        for (int i = 0; i < 2; ++i)
+          packed[i] = pack_e4m3x4(sat448(quotient(bf16_lo(ws[2 * i]), FAST_)),
+                                  sat448(quotient(bf16_hi(ws[2 * i]), FAST_)),
+                                  sat448(quotient(bf16_lo(ws[2 * i + 1]), FAST_)),
+                                  sat448(quotient(bf16_hi(ws[2 * i + 1]), FAST_)));
         if (ok[k]) {
           const int64_t row = rb * 32 + 4 * k + rsub;
           *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
@@ -160,17 +149,13 @@ __global__ void __launch_bounds__(256) quantize_tg_kernel(const uint16_t* __rest
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       m = fmaxf(m, __shfl_xor(m, 2, 64));
       sk[k] = m / 448.0f;
-      const bool recip = m >= 0x1p-60f;
+      const bool recip = m >= QUANT_RECIP_MIN_AMAX;
       rk[k] = recip ? 1.0f / sk[k] : 0.0f;
       all_recip = all_recip && recip;
     }
     auto quotient = [&](float xv, int k, auto FAST_) __attribute__((always_inline)) -> float {
-      if (decltype(FAST_)::value || rk[k] != 0.0f) {
-        const float q0 = xv * rk[k];
-        const float e = __builtin_fmaf(-q0, sk[k], xv);
-        return __builtin_copysignf(__builtin_fmaf(e, rk[k], q0), xv);
-      }
-      return sk[k] != 0.0f ? xv / sk[k] : 0.0f;
+      if (decltype(FAST_)::value || rk[k] != 0.0f) return quant_quotient_recip(xv, sk[k], rk[k]);
+      return quant_quotient_div(xv, sk[k]);
     };
     auto encode_store = [&](auto FAST_) __attribute__((always_inline)) {
 #pragma unroll
@@ -178,15 +163,11 @@ __global__ void __launch_bounds__(256) quantize_tg_kernel(const uint16_t* __rest
         const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
         uint32_t packed[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const float t0 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i]), k, FAST_), -448.0f), 448.0f);
-          const float t1 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i]), k, FAST_), -448.0f), 448.0f);
-          const float t2 = fminf(fmaxf(quotient(bf16_lo(ws[2 * i + 1]), k, FAST_), -448.0f), 448.0f);
-          const float t3 = fminf(fmaxf(quotient(bf16_hi(ws[2 * i + 1]), k, FAST_), -448.0f), 448.0f);
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, wd, true);
-          packed[i] = (uint32_t)wd;
-        }
+        for (int i = 0; i < 2; ++i)
+          packed[i] = pack_e4m3x4(sat448(quotient(bf16_lo(ws[2 * i]), k, FAST_)),
+                                  sat448(quotient(bf16_hi(ws[2 * i]), k, FAST_)),
+                                  sat448(quotient(bf16_lo(ws[2 * i + 1]), k, FAST_)),
+                                  sat448(quotient(bf16_hi(ws[2 * i + 1]), k, FAST_)));
         if (ok[k]) {
           const int64_t row = rb * 32 + 4 * k + rsub;
           *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);

@@ -13,6 +13,10 @@ Recipe (stated once, used everywhere):
   * "N(0, s)" means standard deviation s;
   * prefill activations carry outliers: an independent Bernoulli(0.01) mask
     multiplies the affected fp32 draws by 50 before the bf16 rounding;
+  * the norm workloads (residual add + RMSNorm + token-group quantization
+    ahead of the GEMM, hidden size d = K = 8192) draw the layer output x as
+    N(0, 1) with the same outliers, the residual stream as N(0, 1) and the
+    norm weight gamma as 1 + N(0, 0.1);
   * grouped workloads draw group sizes in 32-row units from a multinomial over
     the non-empty groups (two groups, chosen by the seeded generator, are forced
     empty), so the stacked A has exactly the stated row count.
@@ -24,7 +28,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-T_A, T_B, T_OUTLIER, T_GROUPS, T_EXTRA = 0, 1, 2, 3, 4
+T_A, T_B, T_OUTLIER, T_GROUPS, T_EXTRA, T_RESIDUAL, T_GAMMA = 0, 1, 2, 3, 4, 5, 6
 
 
 def rng_for(seed: int, tensor_id: int) -> np.random.Generator:
@@ -131,3 +135,38 @@ def decode(M: int, N: int) -> Workload:
 def grouped() -> Workload:
     return Workload("grouped-G16-M8192-K7168-N4096", 4, 8192, 4096, 7168, a_std=1.0, b_std=0.02, groups=16)
 
+
+
+@dataclass
+class NormWorkload:
+    """Rows of a residual add + RMSNorm feeding the GEMM's activations."""
+    name: str
+    index: int
+    rows: int
+    d: int
+    eps: float = 1e-6
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    def x_bits(self) -> np.ndarray:
+        return normal_bf16(self.seed, T_A, self.rows, self.d, 1.0, 0.01)
+
+    def residual_bits(self) -> np.ndarray:
+        return normal_bf16(self.seed, T_RESIDUAL, self.rows, self.d, 1.0)
+
+    def gamma_bits(self) -> np.ndarray:
+        g = rng_for(self.seed, T_GAMMA).standard_normal(self.d, dtype=np.float32)
+        return f32_to_bf16_bits(np.float32(1.0) + g * np.float32(0.1))
+
+
+def norm_prefill() -> NormWorkload:
+    return NormWorkload("rmsnorm-M8192-d8192", 5, 8192, 8192)
+
+
+def norm_decode(M: int) -> NormWorkload:
+    """The first M rows of the 64-row draw equal the M-row draw (row-major)."""
+    if M not in (1, 8, 32, 64):
+        raise ValueError(M)
+    return NormWorkload(f"rmsnorm-M{M}-d8192", 6, M, 8192)

@@ -164,6 +164,34 @@ fp8bs_status fp8bs_gemm_tg(const void* a, const float* sa_rows, const void* b, c
 fp8bs_status fp8bs_gemm_tg_nt(const void* a, const float* sa_rows, const void* bt, const float* sbt, void* c_bf16,
                               int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * fp8bs_rmsnorm_quantize_tg - residual add + RMSNorm + per-token-group E4M3
+ *   quantization in one pass over each row.  The norm is [DET part 三,
+ *   section 1]: per row, y = x / sqrt(mean(x^2) + eps) * gamma; section 2 lists
+ *   the residual ("fused add") form and the fusion of the norm with
+ *   per-token-group FP8 quantization.  Per row of d columns:
+ *     residual != NULL:  h = bf16(x + residual), written back to residual
+ *                        (one round-to-nearest-even of the exact sum)
+ *     residual == NULL:  h = x
+ *     rinv = 1 / sqrt(sum(h^2) / d + eps)                       (fp32)
+ *     y_i  = bf16((h_i * rinv) * gamma_i)                       (fp32, then RNE)
+ *     q, scales = fp8bs_quantize_tg of y (1 x 32 groups, bit for bit)
+ *   The sum of squares has a fixed order that depends on d only (never on
+ *   rows), so each row's outputs depend on that row alone.
+ *   x        [rows, d] bf16, 16-byte aligned
+ *   residual [rows, d] bf16 in/out, or NULL; must not overlap x
+ *   gamma    [d] bf16
+ *   eps      finite, >= 0 (else FP8BS_EINVAL); eps == 0 with an all-zero row
+ *            gives NaN scales (precondition: not both)
+ *   q        [rows, d] E4M3 out; scales [rows, d/32] fp32 out
+ *   y        [rows, d] bf16 out (the normalised rows), or NULL to skip it
+ *   d % 32 == 0 and d <= 16384 (else FP8BS_ESHAPE); rows == 0 or d == 0: no-op.
+ *   Outputs must not overlap inputs (residual is updated in place by design).
+ */
+fp8bs_status fp8bs_rmsnorm_quantize_tg(const void* x_bf16, void* residual_bf16, const void* gamma_bf16, float eps,
+                                       int64_t rows, int64_t d, void* q_e4m3, float* scales, void* y_bf16,
+                                       void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8bs_status_str(fp8bs_status status);
 

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = _declared_functions()
     assert names == ["fp8bs_gemm", "fp8bs_gemm_nt", "fp8bs_gemm_tg", "fp8bs_gemm_tg_nt", "fp8bs_grouped_gemm",
-                     "fp8bs_grouped_gemm_nt", "fp8bs_quantize", "fp8bs_quantize_tg", "fp8bs_status_str"]
+                     "fp8bs_grouped_gemm_nt", "fp8bs_quantize", "fp8bs_quantize_tg", "fp8bs_rmsnorm_quantize_tg",
+                     "fp8bs_status_str"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -91,6 +92,29 @@ def test_grouped_argument_checks(g):
     assert g(A16, A4, A16, A4, A4, 2, A16, 64, 40, 64) == ESHAPE
     assert g(A16, A4, A16, A4, A4, 2, A16, 0, 64, 64) == OK           # empty
     assert g(A16, A4, A16, A4, A4, 2, None, 64, 64, 64) == EINVAL
+
+
+def test_rmsnorm_quantize_argument_checks():
+    r = binding.rmsnorm_quantize_tg_raw
+    # x, residual, gamma, eps, rows, d, q, scales, y
+    assert r(A16, None, A16, 1e-6, 0, 64, A16, A4, None) == OK            # empty: no-op
+    assert r(A16, None, A16, 1e-6, 4, 0, A16, A4, None) == OK
+    assert r(A16, None, A16, 1e-6, -1, 64, A16, A4, None) == EINVAL
+    assert r(A16, None, A16, -1.0, 4, 64, A16, A4, None) == EINVAL        # eps < 0
+    assert r(A16, None, A16, float("nan"), 4, 64, A16, A4, None) == EINVAL
+    assert r(A16, None, A16, float("inf"), 4, 64, A16, A4, None) == EINVAL
+    assert r(A16, None, A16, 1e-6, 4, 48, A16, A4, None) == ESHAPE        # d % 32
+    assert r(A16, None, A16, 1e-6, 4, 16384 + 32, A16, A4, None) == ESHAPE  # d too large
+    assert r(None, None, A16, 1e-6, 4, 64, A16, A4, None) == EINVAL
+    assert r(A16, None, None, 1e-6, 4, 64, A16, A4, None) == EINVAL
+    assert r(A16, None, A16, 1e-6, 4, 64, None, A4, None) == EINVAL
+    assert r(A16, None, A16, 1e-6, 4, 64, A16, None, None) == EINVAL
+    assert r(A16 + 2, None, A16, 1e-6, 4, 64, A16, A4, None) == EALIGN
+    assert r(A16, A16 + 8, A16, 1e-6, 4, 64, A16, A4, None) == EALIGN     # residual
+    assert r(A16, None, A16 + 4, 1e-6, 4, 64, A16, A4, None) == EALIGN
+    assert r(A16, None, A16, 1e-6, 4, 64, A16 + 8, A4, None) == EALIGN
+    assert r(A16, None, A16, 1e-6, 4, 64, A16, A4 + 2, None) == EALIGN
+    assert r(A16, None, A16, 1e-6, 4, 64, A16, A4, A16 + 8) == EALIGN     # y
 
 
 def test_tensor_api_rejects_bad_inputs_without_gpu():
