@@ -15,6 +15,8 @@ Also measured (same run, reported under "detail"):
   * the quantizer alone (HBM bytes per launch over its time);
   * the same for per-token-group (1 x 32) activation scales: quantizer, square
     GEMM and the decode sweep in both weight layouts;
+  * the fused residual add + RMSNorm + token-group quantizer at d = 8192
+    (8192 rows, and 1 / 8 / 64 rows);
   * the CPU oracle on a bounded sample of the same workload ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
@@ -134,6 +136,31 @@ def main():
                 flush()
                 fp8bs.gemm(dqa, dsa, dqb, dsb)
             del da, db, dqa, dsa, dqb, dsb
+        # the same decode shapes with the weight K-major
+        for n_dec in (8192, 28672):
+            dwl = W.decode(8, n_dec)
+            dqa, dsa = fp8bs.quantize(to_dev_bf16(dwl.a_bits()))
+            dqbt, dsbt = fp8bs.quantize(to_dev_bf16(np.ascontiguousarray(dwl.b_bits().T)))
+            for _ in range(3):
+                flush()
+                fp8bs.gemm_nt(dqa, dsa, dqbt, dsbt)
+            del dqa, dsa, dqbt, dsbt
+        # token-group activation scales on the square workload
+        sa_tg = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            flush()
+            fp8bs.quantize_tg(a, qa, sa_tg)
+            flush()
+            fp8bs.gemm_tg(qa, sa_tg, qb, sb, out=c)
+        del sa_tg
+        # fused residual add + RMSNorm + token-group quantizer, 8192 x 8192
+        nwl = W.norm_prefill()
+        nx, nr = to_dev_bf16(nwl.x_bits()), to_dev_bf16(nwl.residual_bits())
+        ng = to_dev_bf16(nwl.gamma_bits())
+        for _ in range(3):
+            flush()
+            fp8bs.rmsnorm_quantize_tg(nx, ng, nwl.eps, residual=nr)
+        del nx, nr, ng
         # plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
         dst = torch.empty_like(src)
@@ -240,6 +267,27 @@ def main():
             "decode": decode_sweep(False, True),
         }
         del sa_tg
+
+        # fused residual add + RMSNorm + token-group quantizer, d = 8192: bytes =
+        # x, residual in and out (bf16), codes, scales per row, gamma once
+        norm = []
+        for nwl in (W.norm_prefill(), W.norm_decode(64)):
+            nx, nr = to_dev_bf16(nwl.x_bits()), to_dev_bf16(nwl.residual_bits())
+            ng = to_dev_bf16(nwl.gamma_bits())
+            nq = torch.empty((nwl.rows, nwl.d), dtype=torch.uint8, device=dev)
+            ns = torch.empty((nwl.rows, nwl.d // 32), dtype=torch.float32, device=dev)
+            for m in ((nwl.rows,) if nwl.rows > 64 else (1, 8, 64)):
+                fn = (lambda m=m: fp8bs.rmsnorm_quantize_tg(nx[:m], ng, nwl.eps, residual=nr[:m], q=nq[:m],
+                                                            scales=ns[:m]))
+                for _ in range(3):
+                    fn()
+                n_med, _, _ = time_launch(fn, reps)
+                nbytes = m * (7 * nwl.d + 4 * (nwl.d // 32)) + 2 * nwl.d
+                norm.append({"rows": m, "d": nwl.d, "median_us": round(n_med * 1e3, 2),
+                             "gbs": round(nbytes / (n_med * 1e-3) / 1e9, 1),
+                             "frac_hbm_peak": round(nbytes / (n_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            del nx, nr, ng, nq, ns
+        detail["rmsnorm_residual_quantize_tg"] = norm
 
         # prefill M = K = 8192, N = 28672 and the grouped workload (GEMM only)
         pwl = W.prefill(28672)

@@ -66,6 +66,14 @@ __global__ void __launch_bounds__(256) rmsnorm_quant_tg_kernel(const uint16_t* _
       ok[i] = row_ok && col < d;
       h[i] = ok[i] ? *reinterpret_cast<const uint4*>(xr + col) : make_uint4(0, 0, 0, 0);
     }
+    // gamma is loaded with the row, before the reduction: a row's latency then
+    // holds one round trip to memory, not two
+    uint4 gv[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int64_t col = (int64_t)(WPR * i + wk) * 512 + lane * 8;
+      gv[i] = ok[i] ? *reinterpret_cast<const uint4*>(gamma + col) : make_uint4(0, 0, 0, 0);
+    }
     if (res != nullptr) {
       uint16_t* rr = res + rrow * d;
       uint4 rv[NL];
@@ -114,7 +122,7 @@ __global__ void __launch_bounds__(256) rmsnorm_quant_tg_kernel(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int64_t col = (int64_t)(WPR * i + wk) * 512 + lane * 8;
-      const uint4 g = ok[i] ? *reinterpret_cast<const uint4*>(gamma + col) : make_uint4(0, 0, 0, 0);
+      const uint4 g = gv[i];
       const uint32_t* hw = reinterpret_cast<const uint32_t*>(&h[i]);
       const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
       uint32_t yw[4];

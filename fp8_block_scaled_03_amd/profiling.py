@@ -54,13 +54,17 @@ def _counter(path: str, counter: str):
     return per
 
 
-def traffic_summary(fetch: str, write: str, kernel: str, copy_bytes: int, cmd: str) -> str:
+def traffic_summary(fetch: str, write: str, kernel: str, copy_bytes: int, cmd: str,
+                    sources=GEMM_SOURCES) -> str:
     f = _counter(fetch, "FETCH_SIZE")
     w = _counter(write, "WRITE_SIZE")
     copy_name = [k for k in f if "copyBuffer" in k][0]
     f_factor = statistics.median(f[copy_name]) * 1024 / copy_bytes
     w_factor = statistics.median(w[copy_name]) * 1024 / copy_bytes
-    name = [k for k in f if k.endswith(kernel)][0]
+    name = [k for k in f if k.endswith(kernel)]
+    if len(name) != 1:
+        raise ValueError(f"kernel {kernel!r} matches {name}")
+    name = name[0]
     fk = statistics.median(f[name])
     wk = statistics.median(w[name])
     read_b = fk * 1024 / f_factor
@@ -70,7 +74,8 @@ def traffic_summary(fetch: str, write: str, kernel: str, copy_bytes: int, cmd: s
         "# each divided by what the counter reads for a plain device copy of known size in the same run.",
         f"# command: {cmd}",
         f"kernel: {kernel}",
-        f"source_sha: {source_sha()}",
+        f"source_sha: {source_sha(sources)}",
+        f"sources: {' '.join(sources)}",
         f"copy_bytes: {copy_bytes}",
         f"fetch_factor: {f_factor:.4f}",
         f"write_factor: {w_factor:.4f}",
@@ -111,11 +116,13 @@ def main():
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--cmd", required=True)
+    t.add_argument("--sources", nargs="+", default=GEMM_SOURCES,
+                   help="files whose hash ties the figure to the profiled kernel")
     a = p.parse_args()
     if a.what == "stats":
         print(stats_summary(a.csv, a.cmd), end="")
     else:
-        print(traffic_summary(a.fetch, a.write, a.kernel, a.copy_bytes, a.cmd), end="")
+        print(traffic_summary(a.fetch, a.write, a.kernel, a.copy_bytes, a.cmd, a.sources), end="")
 
 
 if __name__ == "__main__":
