@@ -291,8 +291,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- prologue: K-blocks 0 and 1 staged in LDS, K-block 2 in registers,
-  // K-block 0's fragments in registers
+  // ---- prologue: K-blocks 0 and 1 staged in LDS, K-blocks 2 and 3 in the two
+  // register sets, K-block 0's fragments in registers
   // K = 0: no operand or scale is touched (the caller may pass null pointers);
   // the accumulators stay zero.
   if (KB > 0) {
@@ -307,6 +307,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
   if (KB > 1) { load_stage(1, ra, rb); store_stage(1, ra, rb); }
   if (KB > 0) load_stage(KB > 2 ? 2 : KB - 1, ra, rb);
+  uint4 ra2 = make_uint4(0, 0, 0, 0), rb2 = make_uint4(0, 0, 0, 0);
+  if (KB > 0) load_stage(KB > 3 ? 3 : KB - 1, ra2, rb2);
   __syncthreads();
   v8bf af[4], bfrag[8];
   if (KB > 0) {
@@ -332,7 +334,10 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     if constexpr (TG) read_tg_scales(0, sa4, sbs);
     else read_scales(0, s_cur);
   }
-  for (int kb = 0; kb < KB; ++kb) {
+  // Two register sets alternate between iterations: the global loads of a
+  // K-block are issued two iterations before its staging, so their latency
+  // hides behind two iterations of MFMAs.
+  auto iteration = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
     // next window of scales: written now, first read SCW (SCWT) iterations later
     const bool tg_refill = TG && kb % SCWT == 0 && kb + SCWT < KB;
     if constexpr (TG) {
@@ -371,7 +376,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
         // new register contents alive together.  Past the end the stage written
         // is never read.
         store_stage(sf, ra, rb);
-        load_stage(kb + 3 < KB ? kb + 3 : KB - 1, ra, rb);
+        load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
       }
       if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
@@ -383,6 +388,10 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     __syncthreads();
     sn = sn == 2 ? 0 : sn + 1;
     sf = sf == 2 ? 0 : sf + 1;
+  };
+  for (int kb = 0; kb < KB; kb += 2) {
+    iteration(kb, ra, rb);
+    if (kb + 1 < KB) iteration(kb + 1, ra2, rb2);
   }
 
   // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
