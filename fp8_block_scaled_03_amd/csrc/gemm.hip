@@ -971,6 +971,204 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
 }
 
 // ------------------------------------------------------------------------------------
+// small-M kernel, K-major weight, K-blocks split over the waves
+// ------------------------------------------------------------------------------------
+// When the workgroup's slice has fewer 16x16 output sub-tiles than waves,
+// owning whole sub-tiles leaves most waves idle while the owners form eight K-blocks of
+// partials per round.  Here every wave forms the partials of one K-block of the
+// round for all sub-tiles (phase 1) and parks them in LDS; in the next round
+// all 512 lanes promote them, each lane owning whole output elements and
+// running their chain over the round's K-blocks in ascending order with the
+// same fma(P, sa*sb, acc) as every other kernel (phase 2).  The partials are
+// the same MFMA results, so every bit of C is unchanged.  Refills target the
+// slot of two rounds back: phase 2 still reads the scale records of the
+// previous round's slot.
+template <int MT, int NCB, bool TG = false>
+struct SmallMNtSplitCfg {
+  static constexpr int W = 32 * NCB;
+  static constexpr int CS = 2 * NCB;
+  static constexpr int T = MT * CS;                   // output sub-tiles of the workgroup
+  static constexpr int EPL = T * 256 / STHREADS;      // output elements per lane
+  static constexpr int ACH = (MT + 1) / 2;
+  static constexpr int A_OFF = W * 256;
+  static constexpr int SC_OFF = A_OFF + 16 * MT * 256;  // the 16*MT A rows the fragments read
+  static constexpr int REC = TG ? 512 : 256;
+  static constexpr int SLOT = SC_OFF + SWAVES * REC;
+  static constexpr int PB_BYTES = 2 * SWAVES * T * 1024;  // partials of two rounds
+  static constexpr int D_FIT = (SMALL_LDS_BUDGET - PB_BYTES) / SLOT;
+  static constexpr int D = D_FIT > 8 ? 8 : D_FIT;
+  static constexpr int PB_OFF = D * SLOT;
+  static constexpr int LDS = PB_OFF + PB_BYTES;
+  static_assert(T * 256 % STHREADS == 0, "whole elements per lane");
+  static_assert(D >= 3, "ring too shallow");
+  static_assert(LDS <= SMALL_LDS_BUDGET, "LDS budget");
+  static_assert((D - 3) * (NCB + ACH + (TG ? 2 : 1)) < 64, "vmcnt range");
+};
+
+template <int MT, int NCB, bool TG>
+__global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const uint8_t* __restrict__ a,
+                                                                        const float* __restrict__ sa,
+                                                                        const uint8_t* __restrict__ bt,
+                                                                        const float* __restrict__ sbt,
+                                                                        uint16_t* __restrict__ c, int64_t M,
+                                                                        int64_t N, int64_t K) {
+  using Cfg = SmallMNtSplitCfg<MT, NCB, TG>;
+  constexpr int D = Cfg::D, W = Cfg::W, CS = Cfg::CS, T = Cfg::T, EPL = Cfg::EPL;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const int KB = (int)(K >> 5);
+  const int64_t n0 = (int64_t)blockIdx.x * W;
+  const int cb0 = (int)(n0 >> 5);
+
+  // ---- direct loads of round r (as in gemm_smallm_nt_kernel): weight pieces of
+  // rows 4*(w*NCB+i).., A pieces of rows 4*(w+8*ch).. (only pieces with a row < M),
+  // and the scale record of K-block 8r+w
+  const int lp = lane & 15;
+  const uint8_t* b_row[NCB];
+  int b_g[NCB];
+#pragma unroll
+  for (int i = 0; i < NCB; ++i) {
+    const int r = 4 * (w * NCB + i) + (lane >> 4);
+    b_row[i] = bt + (n0 + r) * K;
+    b_g[i] = lp ^ (r & 15);
+  }
+  const uint8_t* a_row[Cfg::ACH];
+  int a_g[Cfg::ACH];
+  int a_live = 0;
+#pragma unroll
+  for (int ch = 0; ch < Cfg::ACH; ++ch) {
+    const int r = 4 * (w + 8 * ch) + (lane >> 4);
+    const int64_t rr = r < M ? r : M - 1;
+    a_row[ch] = a + rr * K;
+    a_g[ch] = lp ^ (r & 15);
+    a_live += 4 * (w + 8 * ch) < M ? 1 : 0;
+  }
+  const int nrb = (int)((M + 31) >> 5);
+  const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
+  const float* const sc_src =
+      lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sbt + (int64_t)(cb0 + sbj) * KB;
+  const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
+  const float* const tg_sb_src = sbt + (int64_t)(cb0 + (lane < NCB ? lane : NCB - 1)) * KB;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
+
+  auto koff = [&](int r, int g) __attribute__((always_inline)) -> int64_t {
+    int kb = r * SWAVES + (g >> 1);
+    kb = kb < KB ? kb : KB - 1;
+    return (int64_t)kb * 32 + (g & 1) * 16;
+  };
+  auto issue = [&](int r) __attribute__((always_inline)) {
+    const uint32_t sl = ring + (r % D) * Cfg::SLOT;
+#pragma unroll
+    for (int i = 0; i < NCB; ++i) dma16(b_row[i] + koff(r, b_g[i]), sl + (w * NCB + i) * 1024);
+#pragma unroll
+    for (int ch = 0; ch < Cfg::ACH; ++ch)
+      if (ch < a_live) dma16(a_row[ch] + koff(r, a_g[ch]), sl + Cfg::A_OFF + (w + 8 * ch) * 1024);
+    int kc = r * SWAVES + w;
+    kc = kc < KB ? kc : KB - 1;
+    if constexpr (TG) {
+      dma4(tg_sa_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+      dma4(tg_sb_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC + 256);
+    } else {
+      dma4(sc_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+    }
+  };
+
+  const int fr_half = ((lane >> 4) & 1) * 8, fr_hi = lane >> 5;
+  auto frag_off = [&](int row, int q) __attribute__((always_inline)) {
+    return row * 256 + 16 * ((2 * q + fr_hi) ^ (lane & 15)) + fr_half;
+  };
+
+  // phase 1: this wave's K-block (q = w) of round r, every sub-tile t = i*CS + cs
+  auto phase1 = [&](int r) __attribute__((always_inline)) {
+    const unsigned char* sl = smem + (r % D) * Cfg::SLOT;
+    v2i braw[CS], araw[MT];
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) braw[cs] = *reinterpret_cast<const v2i*>(sl + frag_off(16 * cs + (lane & 15), w));
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      araw[i] = *reinterpret_cast<const v2i*>(sl + Cfg::A_OFF + frag_off(16 * i + (lane & 15), w));
+    v8bf bf[CS], af[MT];
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) bf[cs] = e4m3x8_to_bf16x8(braw[cs]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) af[i] = e4m3x8_to_bf16x8(araw[i]);
+    unsigned char* pb = smem + Cfg::PB_OFF + ((r & 1) * SWAVES + w) * T * 1024;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) {
+        const v4f p = TG ? mfma_partial(bf[cs], af[i]) : mfma_partial(af[i], bf[cs]);
+        *reinterpret_cast<v4f*>(pb + (i * CS + cs) * 1024 + lane * 16) = p;
+      }
+  };
+
+  // phase 2: lane G = 64w + lane owns elements e = G + 512j of the workgroup's
+  // T*256 (sub-tile e >> 8, MFMA output slot e & 255)
+  const int G = w * 64 + lane;
+  float acc[EPL];
+  int e_row[EPL], e_col[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    acc[j] = 0.0f;
+    const int e = G + STHREADS * j, t = e >> 8, f = e & 255;
+    const int l = f >> 2, i4 = f & 3;
+    const int row_in = TG ? (l & 15) : 4 * (l >> 4) + i4;
+    const int col_in = TG ? 4 * (l >> 4) + i4 : (l & 15);
+    e_row[j] = 16 * (t / CS) + row_in;
+    e_col[j] = 16 * (t % CS) + col_in;
+  }
+  auto phase2 = [&](int r, int nkb) __attribute__((always_inline)) {
+    const unsigned char* sl = smem + (r % D) * Cfg::SLOT;
+    const unsigned char* pb = smem + Cfg::PB_OFF + (r & 1) * SWAVES * T * 1024;
+#pragma unroll
+    for (int q = 0; q < SWAVES; ++q) {
+      if (q < nkb) {
+        const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF + q * Cfg::REC);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = G + STHREADS * j;
+          const float p = *reinterpret_cast<const float*>(pb + (q * T + (e >> 8)) * 1024 + (e & 255) * 4);
+          const int own_cb = e_col[j] >> 5;
+          const float sc = (TG ? scr[e_row[j]] : scr[e_row[j] >> 5]) * scr[(TG ? 64 : 2) + own_cb];
+          acc[j] = __builtin_fmaf(p, sc, acc[j]);
+        }
+      }
+    }
+  };
+
+  const int rounds = (KB + SWAVES - 1) / SWAVES;
+  if (KB > 0) {
+#pragma unroll
+    for (int d = 0; d < D - 2; ++d) issue(d);
+  }
+  for (int r = 0; r < rounds; ++r) {
+    // this wave's round-r loads have landed: NCB + a_live + scale loads per round, D - 3 rounds may be pending
+    constexpr int LB = (D - 3) * (NCB + (TG ? 2 : 1));
+    if (a_live == 0) wait_vmcnt<LB>();
+    else if (a_live == 1) wait_vmcnt<LB + (D - 3)>();
+    else wait_vmcnt<LB + 2 * (D - 3)>();
+    lds_barrier();   // round r visible; round r-1's partials visible; round r-2's slot free
+    issue(r + D - 2);
+    phase1(r);
+    if (r > 0) phase2(r - 1, SWAVES);   // only the last round can be partial
+  }
+  if (rounds > 0) {
+    lds_barrier();
+    phase2(rounds - 1, KB - (rounds - 1) * SWAVES);
+  }
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int64_t row = e_row[j];
+    if (row < M) c[row * N + n0 + e_col[j]] = (uint16_t)bf16_rne(acc[j]);
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------
 // act_tg: A's scales are per token group, [M, K/32], instead of [ceil(M/32), K/32].
@@ -1038,10 +1236,22 @@ int smallm_nt_ncb(int64_t N) {
   return best;
 }
 
+// 32-column K-major slices with at most 16 rows (two sub-tiles, six of eight
+// waves idle in gemm_smallm_nt_kernel) use the split kernel: 25.3 against
+// 27.3 us at N = K = 8192.  With four sub-tiles the parked partials leave
+// room for only four or five ring slots, which costs more than the idle
+// waves (35.8 against 29.8 us at M = 32).
+template <int MT, int NCB>
+constexpr bool kNtSplit = MT * 2 * NCB <= 2;
+
 template <int MT, int NCB, bool NT, bool TG>
 static void launch_smallm_t(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, uint16_t* c,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if constexpr (NT) {
+  if constexpr (NT && kNtSplit<MT, NCB>) {
+    using Cfg = SmallMNtSplitCfg<MT, NCB, TG>;
+    hipLaunchKernelGGL((gemm_smallm_nt_split_kernel<MT, NCB, TG>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS),
+                       Cfg::LDS, stream, a, sa, b, sb, c, M, N, K);
+  } else if constexpr (NT) {
     using Cfg = SmallMNtCfg<MT, NCB, TG>;
     hipLaunchKernelGGL((gemm_smallm_nt_kernel<MT, NCB, TG>), dim3((unsigned)(N / Cfg::W)), dim3(STHREADS), Cfg::LDS,
                        stream, a, sa, b, sb, c, M, N, K);
@@ -1093,8 +1303,13 @@ static hipError_t set_smallm_attr() {
   hipError_t e = hipFuncSetAttribute((const void*)gemm_smallm_kernel<MT, NCB, TG>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, SmallMCfg<MT, NCB, TG>::LDS);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemm_smallm_nt_kernel<MT, NCB, TG>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, SmallMNtCfg<MT, NCB, TG>::LDS);
+  e = hipFuncSetAttribute((const void*)gemm_smallm_nt_kernel<MT, NCB, TG>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, SmallMNtCfg<MT, NCB, TG>::LDS);
+  if (e != hipSuccess) return e;
+  if constexpr (kNtSplit<MT, NCB>)
+    e = hipFuncSetAttribute((const void*)gemm_smallm_nt_split_kernel<MT, NCB, TG>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, SmallMNtSplitCfg<MT, NCB, TG>::LDS);
+  return e;
 }
 
 template <int NCB, bool TG>

@@ -42,6 +42,8 @@ def _assert_tol(c_bits, ref, absref, label):
     (17, 12288, 96),                                     # small-M, 64-column slices
     (40, 28672, 64), (1, 28672, 320),                    # small-M, 128-column slices
     (65, 64, 64),
+    (9, 12288, 96), (16, 12288, 320),                   # K-blocks split over waves, 64-column slices
+    (24, 96, 160), (32, 64, 288),                        # K-blocks split over waves, 17-32 rows
 ])
 def test_gemm_nt_matches_oracle_and_kn_path(M, N, K):
     qa, sa = _quantized(4000 + M, M, K)
