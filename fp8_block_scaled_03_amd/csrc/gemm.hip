@@ -8,22 +8,26 @@
 // 如何让大模型输出确定的结果", part 一 sections 6-7: batch invariance needs a
 // fixed reduction order, no M-dependent split-K).
 //
-// Two kernels:
+// Kernels:
 //  * tile kernel (large M, and the grouped variant): a 512-thread workgroup owns
 //    a 256x256 C tile; eight waves in a 4(M) x 2(N) grid own 64x128 each
 //    (4 x 8 MFMA sub-tiles of 16x16).  Per 32-deep K-block the workgroup
-//    loads 8 KB of A and 8 KB of B (16 bytes per thread each, coalesced),
-//    decodes E4M3 -> bf16 once, and stores the bf16 tiles into a double-buffered
-//    LDS ring with an XOR swizzle so that the fragment reads are free of bank
-//    conflicts (DeepGEMM write-up, section 3.1, makes the same point for shared
-//    memory; section 3.3 for overlapping the next tile's loads with compute).
-//    A fragments are read K-contiguous with ds_read_b128; B is N-contiguous in
-//    memory, so its fragments come from the LDS transpose read ds_read_b64_tr_b16.
-//  * small-M kernel (M <= 64, decode): a workgroup owns a 32-column slice of C
-//    for all rows and all of K.  Its eight waves each form the partials of
-//    different K-blocks (B streamed once from HBM, the op is bandwidth bound),
-//    pass them through LDS, and the promotion chain then runs in ascending
-//    K-block order - the same sequence of roundings as the tile kernel.
+//    loads 8 KB of A and 8 KB of B (16 bytes per thread each, coalesced, two
+//    K-blocks ahead in two register sets), decodes E4M3 -> bf16 once, and
+//    stores the bf16 tiles into a three-stage LDS ring with an XOR swizzle so
+//    that the fragment reads are free of bank conflicts (DeepGEMM write-up,
+//    section 3.1, makes the same point for shared memory; section 3.3 for
+//    overlapping the next tile's loads with compute).  A fragments are read
+//    K-contiguous with ds_read_b128; B is N-contiguous in memory, so its
+//    fragments come from the LDS transpose read ds_read_b64_tr_b16 (a K-major
+//    weight is staged like A instead).
+//  * small-M kernels (M <= 64, decode): a workgroup owns a slice of 32, 64 or
+//    128 columns of C for all rows and all of K and streams its slice of the
+//    weight once, eight K-blocks per round, with direct global->LDS loads into
+//    a ring several rounds deep.  Waves own whole 16x16 output sub-tiles and
+//    run their promotion chains in ascending K-block order; for one-tile
+//    slices of a K-major weight the split kernel instead forms each K-block's
+//    partials on a different wave and promotes them in order one round later.
 #include "common.hpp"
 
 #include <type_traits>

@@ -16,17 +16,26 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMM_SOURCES = ["fp8_block_scaled_03_amd/csrc/gemm.hip", "fp8_block_scaled_03_amd/csrc/common.hpp"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks or empty lines, so that a
+    comment edit does not retire a profile of unchanged code."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_sha(paths=GEMM_SOURCES) -> str:
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
