@@ -47,8 +47,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tile_square4096.txt"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=100)
+    # untimed: about 20 ms of steps, enough for the clocks to settle (a 10-step
+    # warm-up measured ~10% slower steps than the same steps a hundred later)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--reps", type=int, default=50, help="per-kernel timed launches (flushed)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--quick", action="store_true", help="fewer reps, no decode sweep (for profiling)")
