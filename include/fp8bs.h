@@ -93,9 +93,11 @@ fp8bs_status fp8bs_gemm(const void* a, const float* sa, const void* b, const flo
  *   a       [M_total, K] E4M3          sa [M_total/32, K/32] fp32
  *   b       [G, K, N] E4M3             sb [G, K/32, N/32] fp32
  *   offsets [G+1] int32 on the device: 0 = off[0] <= off[1] <= ... <= off[G] = M_total,
- *           every entry a multiple of 32.  Not checked on the host; the kernel
- *           clamps each range into [0, M_total] and treats a decreasing range as
- *           empty, so a bad table gives wrong rows, never an out-of-bounds access.
+ *           every entry a multiple of 32.  Not checked on the host.  The kernel
+ *           clamps each range into [0, M_total], starts it no earlier than the
+ *           previous range's end and treats a range that would run backwards as
+ *           empty, so a bad table gives wrong rows (with unaligned entries also
+ *           wrong scale rows), never an out-of-bounds access.
  *   c       [M_total, N] bf16 out (rows outside every range are left untouched)
  *   1 <= G <= FP8BS_MAX_GROUPS (else FP8BS_EINVAL); M_total, K, N multiples of 32.
  */

@@ -204,3 +204,47 @@ def test_grouped_all_empty_but_one_and_untouched_rows():
     c = gpu_grouped(qa, sa, qb, sb, off)
     ref, absref = oracle.grouped_gemm_ref(qa, sa, qb, sb, off)
     _assert_tol(c, ref, absref, "grouped one live group")
+
+
+def _effective_ranges(off, M_total):
+    """The documented treatment of a bad offsets table: each range clipped to
+    [0, M_total], started no earlier than the previous range's end, and empty
+    when it would run backwards."""
+    out, prev_end = [], 0
+    for g in range(len(off) - 1):
+        s0 = min(max(int(off[g]), 0), M_total)
+        s1 = min(max(int(off[g + 1]), 0), M_total)
+        s0 = max(s0, prev_end)
+        s1 = max(s1, s0)
+        prev_end = s1
+        out.append((s0, s1))
+    return out
+
+
+def test_grouped_bad_offsets_are_clipped_not_faulted():
+    """Negative, decreasing, overlapping and out-of-range entries (multiples of
+    32): every clipped range holds exactly the plain GEMM's rows for its group,
+    rows outside every range are untouched.  An unaligned table runs too (its
+    rows may use the wrong scale rows; the call must only stay in bounds)."""
+    G, K, N, M = 4, 64, 64, 192
+    qa, sa = _quantized(60, M, K)
+    qb = np.stack([_quantized(61 + i, K, N, std=0.02)[0] for i in range(G)])
+    sb = np.stack([_quantized(61 + i, K, N, std=0.02)[1] for i in range(G)])
+    singles = []
+    for gi in range(G):
+        say(f"bad offsets: single GEMM group {gi}")
+        singles.append(gpu_gemm(qa, sa, qb[gi], sb[gi]))
+    sentinel = np.full((M, N), 0x7FC1, np.uint16)
+    for off in ([-64, 64, 32, 320, 128], [32, 32, 96, 64, 160], [0, 192, 0, 192, 0]):
+        off = np.array(off, np.int32)
+        say(f"bad offsets {off.tolist()}")
+        c = gpu_grouped(qa, sa, qb, sb, off, c_init=sentinel)
+        covered = np.zeros(M, bool)
+        for gi, (s0, s1) in enumerate(_effective_ranges(off, M)):
+            if s1 > s0:
+                assert np.array_equal(c[s0:s1], singles[gi][s0:s1]), (off.tolist(), gi)
+                covered[s0:s1] = True
+        assert np.all(c[~covered] == 0x7FC1), off.tolist()
+    say("unaligned offsets")
+    gpu_grouped(qa, sa, qb, sb, np.array([0, 40, 100, 150, 192], np.int32))
+    assert np.array_equal(gpu_gemm(qa, sa, qb[1], sb[1]), singles[1])
