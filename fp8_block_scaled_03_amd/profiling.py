@@ -3,6 +3,8 @@
     python -m fp8_block_scaled_03_amd.profiling stats  STATS_CSV --cmd "<command>"
     python -m fp8_block_scaled_03_amd.profiling traffic --fetch FETCH_CSV --write WRITE_CSV \
         --kernel gemm_tile_kernel --copy-bytes 268435456 --cmd "<command>"
+    python -m fp8_block_scaled_03_amd.profiling counters P1_CSV P2_CSV --kernel KERNEL \
+        --k-blocks KB --cmd "<command>"
 
 ``traffic`` scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
 counters read for a plain device copy of known size in the same run
@@ -101,6 +103,38 @@ def traffic_summary(fetch: str, write: str, kernel: str, copy_bytes: int, cmd: s
     return "\n".join(lines) + "\n"
 
 
+def counters_summary(paths, kernel: str, k_blocks: int, cmd: str) -> str:
+    """SQ counters of one kernel (median over its dispatches) and the ratios
+    derived from them.  GRBM_GUI_ACTIVE is summed over the 8 XCDs and the SQ
+    cycle counters over the 1024 SIMDs, so a fraction of SIMD time is
+    counter / (GRBM_GUI_ACTIVE / 8 * 1024)."""
+    per = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if not _short(r["Kernel_Name"]).endswith(kernel):
+                continue
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in per.items()}
+    lines = ["# rocprofv3 SQ counters (median per dispatch) and ratios derived from them",
+             f"# command: {cmd}", f"kernel: {kernel}", f"source_sha: {source_sha()}"]
+    for k in sorted(med):
+        lines.append(f"{k}: {med[k]:.0f}")
+    waves = med.get("SQ_WAVES", 0.0)
+    if waves:
+        for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+            if name in med:
+                lines.append(f"{name.lower()}_per_wave_per_kblock: {med[name] / waves / k_blocks:.1f}")
+    if "SQ_LDS_BANK_CONFLICT" in med and med.get("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"lds_bank_conflict_share_of_active: {med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.3f}")
+    if med.get("GRBM_GUI_ACTIVE"):
+        simd_cycles = med["GRBM_GUI_ACTIVE"] / 8 * 1024
+        # (SQ_ACTIVE_INST_* read the same as the instruction counts here, so
+        # they give no busy fraction; only the MFMA counter does)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            lines.append(f"mfma_busy_fraction_of_simd_time: {med['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str):
     """Parse a traffic summary; returns a dict of its key: value lines."""
     d = {}
@@ -127,9 +161,16 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--sources", nargs="+", default=GEMM_SOURCES,
                    help="files whose hash ties the figure to the profiled kernel")
+    q = sub.add_parser("counters")
+    q.add_argument("csv", nargs="+")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--k-blocks", type=int, required=True, help="K/32 of the profiled launch")
+    q.add_argument("--cmd", required=True)
     a = p.parse_args()
     if a.what == "stats":
         print(stats_summary(a.csv, a.cmd), end="")
+    elif a.what == "counters":
+        print(counters_summary(a.csv, a.kernel, a.k_blocks, a.cmd), end="")
     else:
         print(traffic_summary(a.fetch, a.write, a.kernel, a.copy_bytes, a.cmd, a.sources), end="")
 
