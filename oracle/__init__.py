@@ -34,6 +34,7 @@ from .gemm import (dequantize, dequantize_token_groups, gemm_ref, gemm_ref_at, g
                    tolerance_bound, bf16_bits_to_f64)
 from .exact import gemm_exact
 from .rmsnorm import residual_add, rmsnorm_ref, rmsnorm_tolerance_ok, RMS_REL_TOL, RMS_ABS_TOL
+from .e8m0 import e8m0_exponent, quantize_blocks_e8m0, dequantize_e8m0, gemm_ref_e8m0_nt
 
 __all__ = [
     "Minifloat", "E4M3FN", "FP16", "BF16",
@@ -45,4 +46,5 @@ __all__ = [
     "tolerance_ok", "tolerance_bound", "bf16_bits_to_f64",
     "gemm_exact",
     "residual_add", "rmsnorm_ref", "rmsnorm_tolerance_ok", "RMS_REL_TOL", "RMS_ABS_TOL",
+    "e8m0_exponent", "quantize_blocks_e8m0", "dequantize_e8m0", "gemm_ref_e8m0_nt",
 ]
