@@ -101,6 +101,33 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float t0, float t1, float t2, fl
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
+// ------------------------------------------------------------------------------------
+// direct global->LDS loads
+// ------------------------------------------------------------------------------------
+// One direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4:
+// lane l's bytes land at M0 + 16*l; M0 = LDS byte address of the wave's 1 KB
+// destination).  Issued from inline asm so that the compiler does not drain
+// every load before the next LDS read; the callers wait with explicit vmcnt
+// counts (a wave's loads complete in issue order).  Nothing else in these
+// kernels uses M0.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
+               : "memory");
+}
+// The same with 4 bytes per lane (lane l's dword lands at M0 + 4*l).
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gptr)
+               : "memory");
+}
+// Workgroup barrier that orders LDS only: the direct loads in flight keep
+// running (a plain __syncthreads would drain them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // A value known to be equal in every lane, moved to a scalar register.
 __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
