@@ -9,7 +9,8 @@ package loads nothing; the first call loads the library and raises
 _BINDING_NAMES = ("Fp8bsError", "quantize", "gemm", "grouped_gemm", "gemm_nt", "grouped_gemm_nt", "quantize_tg",
                   "gemm_tg", "gemm_tg_nt", "library_path", "load_library", "quantize_raw", "gemm_raw",
                   "grouped_gemm_raw", "gemm_nt_raw", "grouped_gemm_nt_raw", "quantize_tg_raw", "gemm_tg_raw",
-                  "gemm_tg_nt_raw", "rmsnorm_quantize_tg", "rmsnorm_quantize_tg_raw")
+                  "gemm_tg_nt_raw", "rmsnorm_quantize_tg", "rmsnorm_quantize_tg_raw",
+                  "quantize_e8m0", "gemm_e8m0_nt", "quantize_e8m0_raw", "gemm_e8m0_nt_raw")
 
 __all__ = list(_BINDING_NAMES)
 

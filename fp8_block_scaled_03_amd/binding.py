@@ -61,6 +61,10 @@ def load_library() -> ctypes.CDLL:
         lib.fp8bs_grouped_gemm_nt.restype = ctypes.c_int
         lib.fp8bs_rmsnorm_quantize_tg.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp, vp]
         lib.fp8bs_rmsnorm_quantize_tg.restype = ctypes.c_int
+        lib.fp8bs_quantize_e8m0.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.fp8bs_quantize_e8m0.restype = ctypes.c_int
+        lib.fp8bs_gemm_e8m0_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.fp8bs_gemm_e8m0_nt.restype = ctypes.c_int
         lib.fp8bs_status_str.argtypes = [ctypes.c_int]
         lib.fp8bs_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -125,6 +129,14 @@ def gemm_tg_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) 
 def rmsnorm_quantize_tg_raw(x_ptr, res_ptr, gamma_ptr, eps, rows, d, q_ptr, s_ptr, y_ptr, stream=None) -> int:
     return load_library().fp8bs_rmsnorm_quantize_tg(x_ptr, res_ptr, gamma_ptr, eps, rows, d, q_ptr, s_ptr, y_ptr,
                                                     stream)
+
+
+def quantize_e8m0_raw(x_ptr, rows, cols, q_ptr, e_ptr, stream=None) -> int:
+    return load_library().fp8bs_quantize_e8m0(x_ptr, rows, cols, q_ptr, e_ptr, stream)
+
+
+def gemm_e8m0_nt_raw(a_ptr, ea_ptr, bt_ptr, ebt_ptr, c_ptr, M, N, K, stream=None) -> int:
+    return load_library().fp8bs_gemm_e8m0_nt(a_ptr, ea_ptr, bt_ptr, ebt_ptr, c_ptr, M, N, K, stream)
 
 
 def gemm_nt_raw(a_ptr, sa_ptr, bt_ptr, sbt_ptr, c_ptr, M, N, K, stream=None) -> int:
@@ -343,3 +355,43 @@ def rmsnorm_quantize_tg(x: torch.Tensor, gamma: torch.Tensor, eps: float, residu
     _check(rmsnorm_quantize_tg_raw(_ptr(x), _ptr(residual), _ptr(gamma), float(eps), R, d, _ptr(q), _ptr(scales),
                                    _ptr(y), _stream_ptr(x)))
     return (q, scales) if y is None else (q, scales, y)
+
+
+def quantize_e8m0(x: torch.Tensor, q: torch.Tensor | None = None, e8m0: torch.Tensor | None = None):
+    """bf16 [R, C] -> (E4M3 codes uint8 [R, C], E8M0 exponent bytes uint8 [ceil(R/32), C/32])."""
+    _need(x, "x", torch.bfloat16, 2)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty(((R + BLOCK - 1) // BLOCK, C // BLOCK), dtype=torch.uint8, device=x.device)
+    _need(q, "q", E4M3_DTYPES, 2)
+    _need(e8m0, "e8m0", torch.uint8, 2)
+    _same_device(x, q, e8m0)
+    if tuple(q.shape) != (R, C) or tuple(e8m0.shape) != ((R + BLOCK - 1) // BLOCK, C // BLOCK):
+        raise ValueError("output shapes do not match the input")
+    _check(quantize_e8m0_raw(_ptr(x), R, C, _ptr(q), _ptr(e8m0), _stream_ptr(x)))
+    return q, e8m0
+
+
+def gemm_e8m0_nt(a: torch.Tensor, ea: torch.Tensor, bt: torch.Tensor, ebt: torch.Tensor,
+                 out: torch.Tensor | None = None):
+    """E4M3 a [M, K] with E8M0 bytes ea [ceil(M/32), K/32], bt [N, K] with ebt [N/32, K/32] -> bf16 [M, N]."""
+    _need(a, "a", E4M3_DTYPES, 2)
+    _need(bt, "bt", E4M3_DTYPES, 2)
+    _need(ea, "ea", torch.uint8, 2)
+    _need(ebt, "ebt", torch.uint8, 2)
+    M, K = a.shape
+    N, K2 = bt.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if tuple(ea.shape) != ((M + BLOCK - 1) // BLOCK, K // BLOCK) or tuple(ebt.shape) != (N // BLOCK, K // BLOCK):
+        raise ValueError("exponent grid shapes do not match the operands")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _same_device(a, ea, bt, ebt, out)
+    _check(gemm_e8m0_nt_raw(_ptr(a), _ptr(ea), _ptr(bt), _ptr(ebt), _ptr(out), M, N, K, _stream_ptr(a)))
+    return out

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8bs.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "rmsnorm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "rmsnorm.hip", "gemm_e8m0.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -26,6 +26,7 @@ fp8bs_status ensure_attributes() {
   std::lock_guard<std::mutex> lock(mu);
   if (!done[dev]) {
     if (fp8bs::set_gemm_attributes() != hipSuccess) return FP8BS_EHIP;
+    if (fp8bs::set_gemm_e8m0_attributes() != hipSuccess) return FP8BS_EHIP;
     done[dev] = true;
   }
   return FP8BS_OK;
@@ -92,6 +93,32 @@ fp8bs_status fp8bs_rmsnorm_quantize_tg(const void* x_bf16, void* residual_bf16, 
     return FP8BS_EALIGN;
   return from_hip(fp8bs::launch_rmsnorm_quantize_tg(x_bf16, residual_bf16, gamma_bf16, eps, rows, d, q_e4m3, scales,
                                                     y_bf16, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_quantize_e8m0(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, void* e8m0,
+                                 void* stream) {
+  if (rows < 0 || cols < 0) return FP8BS_EINVAL;
+  if (rows > MAX_DIM || cols > MAX_DIM) return FP8BS_ESHAPE;
+  if (cols % 32) return FP8BS_ESHAPE;
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x_bf16 || !q_e4m3 || !e8m0) return FP8BS_EINVAL;
+  if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16)) return FP8BS_EALIGN;
+  return from_hip(fp8bs::launch_quantize_e8m0(x_bf16, rows, cols, q_e4m3, e8m0, (hipStream_t)stream));
+}
+
+fp8bs_status fp8bs_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c_bf16,
+                                int64_t M, int64_t N, int64_t K, void* stream) {
+  fp8bs_status st = check_gemm_dims(M, N, K);
+  if (st != FP8BS_OK) return st;
+  if (K % 128) return FP8BS_ESHAPE;
+  if (M == 0 || N == 0) return FP8BS_OK;
+  if (!c_bf16) return FP8BS_EINVAL;
+  if (K > 0 && (!a || !ea || !bt || !ebt)) return FP8BS_EINVAL;
+  if (!aligned(c_bf16, 16) || (K > 0 && (!aligned(a, 16) || !aligned(bt, 16) || !aligned(ea, 4) || !aligned(ebt, 4))))
+    return FP8BS_EALIGN;
+  st = ensure_attributes();
+  if (st != FP8BS_OK) return st;
+  return from_hip(fp8bs::launch_gemm_e8m0_nt(a, ea, bt, ebt, c_bf16, M, N, K, (hipStream_t)stream));
 }
 
 static fp8bs_status gemm_common(const void* a, const float* sa, const void* b, const float* sb, void* c_bf16,

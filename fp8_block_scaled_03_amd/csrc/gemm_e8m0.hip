@@ -1,0 +1,165 @@
+// E4M3 GEMM with power-of-two (E8M0) 32x32 block scales on gfx950's
+// hardware-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
+//
+// C[i,j] = sum_k dec(A[i,k]) 2^Ea[i/32,k/32] * dec(Bt[j,k]) 2^Eb[j/32,k/32]
+// (the DeepGEMM write-up's 32x32 blocks, sections 2.2-2.3, with the scales
+// restricted to powers of two).  One instruction takes 128 K of both operands
+// plus one E8M0 byte per row (or column) and 32-deep K-block, applies the
+// scales and accumulates into C: no decode, no promotion on the VALU.  Its
+// accumulation is not exact: terms far below the instruction's largest
+// product lose bits.  Every kernel of this contract runs the same instruction
+// sequence per element (128-deep steps in ascending K), so results do not
+// depend on M.
+//
+// Operand layout of the instruction (lane l, g = l >> 4): lane l holds row
+// (l & 15) of the 16-row operand, bytes 0-15 = K [16g, 16g+16) and bytes
+// 16-31 = K [64+16g, 64+16g+16); the scale of (row r, 32-deep K-block kb)
+// comes from lane 16*kb + r.  The first operand's rows are C's columns here
+// (the weight), so a lane's four results are four columns of one row.
+//
+// Tile: 128 x 128 per 256-thread workgroup; four waves of 64 x 64 (4 x 4
+// sub-tiles).  A and Bt are streamed as E4M3 bytes with direct global->LDS
+// loads into a three-stage ring of 128-deep K steps; row r of a stage holds its
+// 128 bytes with 16-byte piece p at position p ^ (r & 7).  Each stage also
+// carries the step's scale bytes (four K-blocks for the tile's four A
+// row-blocks and four Bt row-blocks).
+#include "common.hpp"
+
+namespace fp8bs {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+constexpr int EBM = 128, EBN = 128, EBK = 128, ETHREADS = 256, ESTAGES = 3;
+constexpr int E_OPND_BYTES = EBM * EBK;           // 16 KB per operand and stage
+constexpr int E_SC_OFF = 2 * E_OPND_BYTES;        // scale records after A and Bt
+constexpr int E_STAGE = E_SC_OFF + 4 * 256;       // one 256-byte record per wave
+constexpr int E_LDS = ESTAGES * E_STAGE;          // 99 KB
+
+__global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* __restrict__ a,
+                                                                const uint8_t* __restrict__ ea,
+                                                                const uint8_t* __restrict__ bt,
+                                                                const uint8_t* __restrict__ ebt,
+                                                                uint16_t* __restrict__ c, int64_t M, int64_t N,
+                                                                int64_t K, int64_t tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const int wm = w & 1, wn = w >> 1;
+  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int64_t row0 = tm * EBM, col0 = tn * EBN;
+  const int KS = (int)(K / EBK);
+  const int64_t KB = K >> 5;
+
+  // ---- direct loads: wave w fills 1 KB pieces 4w..4w+3 of each operand
+  // (rows 8p..8p+7); lane l loads row 8p + (l >> 3), global piece
+  // (l & 7) ^ (row & 7), so that LDS position l & 7 holds it.  Rows past the
+  // matrix read its last row (never stored).
+  const uint8_t* a_src[4];
+  const uint8_t* b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (w * 4 + i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    int64_t ar = row0 + r, br = col0 + r;
+    ar = ar < M ? ar : M - 1;
+    br = br < N ? br : N - 1;
+    a_src[i] = a + ar * K + chunk * 16;
+    b_src[i] = bt + br * K + chunk * 16;
+  }
+  // scale record: lanes 0-3 the four A row-blocks of the tile, lanes 4-7 the
+  // four Bt row-blocks (clamped); 4 bytes each = the step's four K-blocks
+  const int64_t nrb_a = (M + 31) >> 5, nrb_b = N >> 5;
+  const int sl = lane & 7;
+  int64_t srb = sl < 4 ? (row0 >> 5) + sl : (col0 >> 5) + (sl - 4);
+  const uint8_t* sc_src = sl < 4 ? ea + (srb < nrb_a ? srb : nrb_a - 1) * KB
+                                 : ebt + (srb < nrb_b ? srb : nrb_b - 1) * KB;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
+
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    // the slot follows the step; past the end the last step's bytes are
+    // reloaded into a slot that is never read again
+    const uint32_t slot = ring + (step % ESTAGES) * E_STAGE;
+    const int ks = step < KS ? step : KS - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(a_src[i] + (int64_t)ks * EBK, slot + (w * 4 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(b_src[i] + (int64_t)ks * EBK, slot + E_OPND_BYTES + (w * 4 + i) * 1024);
+    dma4(sc_src + (int64_t)ks * 4, slot + E_SC_OFF + w * 256);
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int g = lane >> 4, lo = lane & 15;
+  auto frag = [&](const unsigned char* base, int r) __attribute__((always_inline)) -> v8i_t {
+    const v4i p0 = *reinterpret_cast<const v4i*>(base + r * EBK + 16 * (g ^ (r & 7)));
+    const v4i p1 = *reinterpret_cast<const v4i*>(base + r * EBK + 16 * ((4 + g) ^ (r & 7)));
+    return v8i_t{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+  };
+
+  // ring: steps ks and ks+1 in flight before step ks is consumed (9 loads per step and wave)
+  if (KS > 0) {
+    issue(0);
+    issue(1);
+  }
+  for (int ks = 0; ks < KS; ++ks) {
+    wait_vmcnt<9>();   // step ks has landed (step ks+1 may still be in flight)
+    lds_barrier();     // ... for every wave; step ks-1's slot is free
+    issue(ks + 2);
+    const unsigned char* slot = smem + (ks % ESTAGES) * E_STAGE;
+    const unsigned char* rec = slot + E_SC_OFF + w * 256;
+    v8i_t af[4], bf[4];
+    int sa_b[4], sb_b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = frag(slot, wm * 64 + 16 * i + lo);
+      sa_b[i] = rec[4 * (2 * wm + (i >> 1)) + g];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf[j] = frag(slot + E_OPND_BYTES, wn * 64 + 16 * j + lo);
+      sb_b[j] = rec[16 + 4 * (2 * wn + (j >> 1)) + g];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0, sb_b[j], 0,
+                                                                       sa_b[i]);
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: lane holds row 16i + (lane & 15), columns 16j + 4g .. +3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + wm * 64 + 16 * i + lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = col0 + wn * 64 + 16 * j + 4 * g;
+      if (row < M && col < N) {
+        const uint32_t w0 = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        const uint32_t w1 = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(c + row * N + col) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+hipError_t set_gemm_e8m0_attributes() {
+  return hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, E_LDS);
+}
+
+hipError_t launch_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c, int64_t M,
+                               int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t tiles_m = (M + EBM - 1) / EBM, tiles_n = (N + EBN - 1) / EBN;
+  hipLaunchKernelGGL(gemm_e8m0_nt_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(ETHREADS), E_LDS, stream,
+                     (const uint8_t*)a, (const uint8_t*)ea, (const uint8_t*)bt, (const uint8_t*)ebt, (uint16_t*)c,
+                     M, N, K, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace fp8bs

@@ -24,6 +24,11 @@ hipError_t set_gemm_attributes();
 hipError_t launch_rmsnorm_quantize_tg(const void* x, void* residual, const void* gamma, float eps, int64_t rows,
                                       int64_t d, void* q, float* scales, void* y, hipStream_t stream);
 int rmsnorm_max_cols();
+// power-of-two (E8M0) block scales: one byte E + 127 per 32x32 block
+hipError_t launch_quantize_e8m0(const void* x, int64_t rows, int64_t cols, void* q, void* e8, hipStream_t stream);
+hipError_t launch_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c, int64_t M,
+                               int64_t N, int64_t K, hipStream_t stream);
+hipError_t set_gemm_e8m0_attributes();
 
 // M at or below which the bandwidth-oriented small-M kernel runs.  Both kernels
 // follow the same per-element recipe, so the switch never changes a result.

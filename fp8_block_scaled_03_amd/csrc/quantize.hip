@@ -180,6 +180,83 @@ __global__ void __launch_bounds__(256) quantize_tg_kernel(const uint16_t* __rest
   }
 }
 
+// Power-of-two (E8M0) scales: per 32x32 block E = the smallest integer with
+// 448 * 2^E >= amax, clamped to [-127, 127] (-127 for a zero block), stored as
+// the byte E + 127; codes E4M3(x * 2^-E), the scaling exact.  With amax =
+// (1 + m) 2^L (L its exponent, m its mantissa fraction), 448 * 2^(L-8) =
+// 1.75 * 2^L, so E = L - 8 when m <= 0.75 and L - 7 otherwise; a subnormal or
+// zero amax (L < -126) lands on the clamp.
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, amax);
+  const int ef = (int)(u >> 23);
+  if (ef == 0) return -127;
+  const int e = ef - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^k for k in [-127, 127] (2^-127 is an fp32 subnormal).
+__device__ __forceinline__ float exp2_int(int k) {
+  return k >= -126 ? __builtin_bit_cast(float, (uint32_t)(k + 127) << 23) : __builtin_bit_cast(float, 0x00400000u);
+}
+
+// The block quantizer's region mapping (one wave per 32 rows x 128 columns).
+__global__ void __launch_bounds__(256) quantize_e8m0_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                            int64_t cols, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ e8, int64_t n_regions) {
+  const int lane = threadIdx.x & 63;
+  const int piece = lane & 15, rsub = lane >> 4;
+  const int b = piece >> 2, cpart = piece & 3;
+  const int64_t cb_count = cols >> 5;
+  const int64_t rg_per_row = (cb_count + Q_BLOCKS - 1) / Q_BLOCKS;
+  const int64_t waves_total = (int64_t)gridDim.x * 4;
+  for (int64_t reg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); reg < n_regions; reg += waves_total) {
+    const int64_t rb = reg / rg_per_row, g = reg - rb * rg_per_row;
+    const int64_t cb = g * Q_BLOCKS + b;
+    const bool cb_ok = cb < cb_count;
+    const int64_t col = (cb_ok ? cb : cb_count - 1) * 32 + cpart * 8;
+    uint4 w[8];
+    bool ok[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t row = rb * 32 + 4 * k + rsub;
+      ok[k] = cb_ok && row < rows;
+      const int64_t rc = row < rows ? row : rows - 1;
+      w[k] = ok[k] ? *reinterpret_cast<const uint4*>(x + rc * cols + col) : make_uint4(0, 0, 0, 0);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ws[i])), fabsf(bf16_hi(ws[i]))));
+    }
+    const int E = e8m0_exponent(block_max(m));
+    const float r = exp2_int(-E);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t ws[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+      uint32_t packed[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        packed[i] = pack_e4m3x4(sat448(bf16_lo(ws[2 * i]) * r), sat448(bf16_hi(ws[2 * i]) * r),
+                                sat448(bf16_lo(ws[2 * i + 1]) * r), sat448(bf16_hi(ws[2 * i + 1]) * r));
+      if (ok[k]) {
+        const int64_t row = rb * 32 + 4 * k + rsub;
+        *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
+      }
+    }
+    if (cpart == 0 && rsub == 0 && cb_ok) e8[rb * cb_count + cb] = (uint8_t)(E + 127);
+  }
+}
+
+hipError_t launch_quantize_e8m0(const void* x, int64_t rows, int64_t cols, void* q, void* e8, hipStream_t stream) {
+  const int64_t n_regions = ((rows + 31) / 32) * ((cols / 32 + Q_BLOCKS - 1) / Q_BLOCKS);
+  int64_t grid = (n_regions + 3) / 4;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(quantize_e8m0_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)x, rows,
+                     cols, (uint8_t*)q, (uint8_t*)e8, n_regions);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_tg(const void* x, int64_t rows, int64_t cols, void* q, float* scales,
                               hipStream_t stream) {
   const int64_t n_regions = ((rows + 31) / 32) * ((cols / 32 + Q_BLOCKS - 1) / Q_BLOCKS);

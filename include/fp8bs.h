@@ -194,6 +194,38 @@ fp8bs_status fp8bs_rmsnorm_quantize_tg(const void* x_bf16, void* residual_bf16, 
                                        int64_t rows, int64_t d, void* q_e4m3, float* scales, void* y_bf16,
                                        void* stream);
 
+/*
+ * Power-of-two (E8M0) block scales.  A separate contract: the DeepGEMM
+ * write-up's 32x32 blocks [DG 2.2, 5.2] with each scale restricted to a power
+ * of two 2^E, stored as one byte E + 127, so that gfx950's hardware-scaled
+ * F8F6F4 MFMA applies it.  The pages describe no such variant.
+ *
+ * fp8bs_quantize_e8m0 - per 32x32 block: E = the smallest integer with
+ *   448 * 2^E >= amax, clamped to [-127, 127] (-127 for an all-zero block);
+ *   codes = E4M3(x * 2^-E) (exact scaling, then round half to even, sign
+ *   kept; no value saturates).
+ *   x [rows, cols] bf16, q [rows, cols] E4M3 out (both 16-byte aligned),
+ *   e8m0 [ceil(rows/32), cols/32] bytes out.  Checks as fp8bs_quantize.
+ */
+fp8bs_status fp8bs_quantize_e8m0(const void* x_bf16, int64_t rows, int64_t cols, void* q_e4m3, void* e8m0,
+                                 void* stream);
+
+/*
+ * fp8bs_gemm_e8m0_nt - C = sum_k dec(A) 2^Ea * dec(Bt) 2^Eb with the weight
+ *   K-major [DG 6], on the hardware-scaled MFMA: 128-deep K steps in ascending
+ *   order, accumulated by the instruction itself.  Results do not depend on M
+ *   (every M runs the same instruction sequence per element).  The
+ *   instruction's accumulation is not exact: a term far below the largest
+ *   product of its 128-deep step can lose bits, so the error depends on the
+ *   data's dynamic range (it is not bounded by the fp8bs_gemm recipe's bound).
+ *   a  [M, K] E4M3, ea  [ceil(M/32), K/32] bytes (4-byte aligned)
+ *   bt [N, K] E4M3, ebt [N/32, K/32] bytes (4-byte aligned)
+ *   c  [M, N] bf16 out.  K % 128 == 0 and N % 32 == 0 (else FP8BS_ESHAPE);
+ *   M == 0 or N == 0: no-op; K == 0: C is filled with +0.
+ */
+fp8bs_status fp8bs_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c_bf16,
+                                int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* fp8bs_status_str(fp8bs_status status);
 

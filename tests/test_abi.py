@@ -17,15 +17,15 @@ A4 = 0x10004
 
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "fp8bs.h")).read()
-    return sorted(set(re.findall(r"\b(fp8bs_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fp8bs_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = binding.load_library()
     names = _declared_functions()
-    assert names == ["fp8bs_gemm", "fp8bs_gemm_nt", "fp8bs_gemm_tg", "fp8bs_gemm_tg_nt", "fp8bs_grouped_gemm",
-                     "fp8bs_grouped_gemm_nt", "fp8bs_quantize", "fp8bs_quantize_tg", "fp8bs_rmsnorm_quantize_tg",
-                     "fp8bs_status_str"]
+    assert names == ["fp8bs_gemm", "fp8bs_gemm_e8m0_nt", "fp8bs_gemm_nt", "fp8bs_gemm_tg", "fp8bs_gemm_tg_nt",
+                     "fp8bs_grouped_gemm", "fp8bs_grouped_gemm_nt", "fp8bs_quantize", "fp8bs_quantize_e8m0",
+                     "fp8bs_quantize_tg", "fp8bs_rmsnorm_quantize_tg", "fp8bs_status_str"]
     for n in names:
         assert hasattr(lib, n), n
 
@@ -92,6 +92,22 @@ def test_grouped_argument_checks(g):
     assert g(A16, A4, A16, A4, A4, 2, A16, 64, 40, 64) == ESHAPE
     assert g(A16, A4, A16, A4, A4, 2, A16, 0, 64, 64) == OK           # empty
     assert g(A16, A4, A16, A4, A4, 2, None, 64, 64, 64) == EINVAL
+
+
+def test_e8m0_argument_checks():
+    q = binding.quantize_e8m0_raw
+    assert q(A16, 0, 64, A16, A4) == OK
+    assert q(A16, 4, 48, A16, A4) == ESHAPE
+    assert q(None, 4, 64, A16, A4) == EINVAL
+    assert q(A16, 4, 64, A16, None) == EINVAL
+    assert q(A16 + 8, 4, 64, A16, A4) == EALIGN
+    g = binding.gemm_e8m0_nt_raw
+    assert g(A16, A4, A16, A4, A16, 0, 64, 128) == OK
+    assert g(A16, A4, A16, A4, A16, 4, 64, 96) == ESHAPE      # K % 128
+    assert g(A16, A4, A16, A4, A16, 4, 40, 128) == ESHAPE     # N % 32
+    assert g(A16, None, A16, A4, A16, 4, 64, 128) == EINVAL
+    assert g(A16, A4, A16, A4 + 1, A16, 4, 64, 128) == EALIGN
+    assert g(A16 + 4, A4, A16, A4, A16, 4, 64, 128) == EALIGN
 
 
 def test_rmsnorm_quantize_argument_checks():

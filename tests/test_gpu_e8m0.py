@@ -1,0 +1,142 @@
+"""Power-of-two (E8M0) block scales on the hardware-scaled MFMA: the quantizer
+bit-exact against the oracle; the GEMM against the oracle within the bound
+below, batch invariant, and exactly scaled by 2^p when every exponent byte
+of A moves by p."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_block_scaled_03_amd as fp8bs
+from fp8_block_scaled_03_amd import workloads as W
+
+from gpu_util import bf16_dev, bits_np, bits_to_f64, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+# The instruction's accumulation drops low bits of terms far below the largest
+# product of a 128-deep step (measured; its exact rule is not documented), so
+# the bound has a larger magnitude-sum term than the exact recipe's 1e-6.
+E8M0_REL, E8M0_ABS_SUM = 2.0 ** -8, 2.0 ** -14
+
+
+def e8m0_ok(c_bits, ref, absref):
+    return np.abs(bits_to_f64(c_bits) - ref) <= E8M0_REL * np.abs(ref) + E8M0_ABS_SUM * absref
+
+
+def gpu_quantize_e8m0(x_bits):
+    q, e = fp8bs.quantize_e8m0(bf16_dev(x_bits))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), e.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols,std", [(1, 32, 1.0), (33, 64, 1e-30), (100, 96, 1e20), (300, 1024, 0.02),
+                                           (64, 8192, 1.0)])
+def test_quantize_e8m0_bit_exact(rows, cols, std):
+    x = W.normal_bf16(8000 + rows, 0, rows, cols, std, 0.01)
+    x[0, :32] = 0                                   # a zero block (with its row block's other rows)
+    if rows > 3:
+        x[3, 40] = 0x8000
+    say(f"quantize_e8m0 {rows}x{cols} std={std}")
+    q, e = gpu_quantize_e8m0(x)
+    qo, eo = oracle.quantize_blocks_e8m0(x)
+    assert np.array_equal(e, eo), "exponents differ"
+    bad = np.argwhere(q != qo)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+def test_quantize_e8m0_all_bf16_under_block_maxima():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    xf = (bits << 16).view(np.float32)
+    allb = bits[np.isfinite(xf)].astype(np.uint16)
+    for amax_bits in (0x43E0, 0x3F80, 0x0001, 0x7F7F, 0x3FE1):
+        af = np.array([np.uint32(amax_bits) << np.uint32(16)], np.uint32).view(np.float32)[0]
+        keep = allb[np.abs((allb.astype(np.uint32) << 16).view(np.float32)) <= af]
+        n = -(-len(keep) // 1023)
+        pad = np.zeros(n * 1023, np.uint16)
+        pad[:len(keep)] = keep
+        blocks = np.concatenate([np.full((n, 1), amax_bits, np.uint16), pad.reshape(n, 1023)], axis=1)
+        x = blocks.reshape(n, 32, 32).transpose(1, 0, 2).reshape(32, n * 32)   # one 32x32 block per group
+        say(f"quantize_e8m0 all bf16 under {amax_bits:#06x}")
+        q, e = gpu_quantize_e8m0(x)
+        qo, eo = oracle.quantize_blocks_e8m0(x)
+        assert np.array_equal(e, eo) and np.array_equal(q, qo), hex(amax_bits)
+
+
+def _operands(seed, M, N, K, a_std=1.0, b_std=0.02, outliers=0.01):
+    qa, ea = oracle.quantize_blocks_e8m0(W.normal_bf16(seed, 0, M, K, a_std, outliers))
+    qbt, ebt = oracle.quantize_blocks_e8m0(W.normal_bf16(seed, 1, N, K, b_std))
+    return qa, ea, qbt, ebt
+
+
+def gpu_gemm_e8m0(qa, ea, qbt, ebt):
+    c = fp8bs.gemm_e8m0_nt(u8_dev(qa), u8_dev(ea), u8_dev(qbt), u8_dev(ebt))
+    torch.cuda.synchronize()
+    return bits_np(c)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (7, 96, 256), (130, 160, 384), (256, 256, 512),
+                                   (300, 1024, 1024), (64, 4096, 2048)])
+def test_gemm_e8m0_matches_oracle(M, N, K):
+    qa, ea, qbt, ebt = _operands(8100 + M, M, N, K)
+    say(f"gemm_e8m0 M={M} N={N} K={K}")
+    c = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    ref, absref = oracle.gemm_ref_e8m0_nt(qa, ea, qbt, ebt)
+    err = np.abs(bits_to_f64(c) - ref)
+    say(f"  max err/|ref| {np.max(err / np.maximum(np.abs(ref), 1e-300)):.3g}  "
+        f"max err/absref {np.max(err / np.maximum(absref, 1e-300)):.3g}")
+    ok = e8m0_ok(c, ref, absref)
+    assert ok.all(), f"{int((~ok).sum())} of {ok.size} outside the bound"
+
+
+def test_gemm_e8m0_rows_independent_of_batch_and_k0():
+    qa, ea, qbt, ebt = _operands(8200, 300, 512, 512)
+    say("gemm_e8m0 invariance full M=300")
+    full = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    # prefixes starting on a 32-row boundary take the matching exponent rows;
+    # a single row takes its block's exponent row
+    for lo, hi in ((0, 1), (0, 7), (64, 96), (32, 160), (299, 300), (100, 101)):
+        say(f"gemm_e8m0 rows {lo}:{hi}")
+        eg = ea[lo // 32:lo // 32 + -(-(hi - lo) // 32)]
+        assert lo % 32 == 0 or hi - lo == 1
+        part = gpu_gemm_e8m0(qa[lo:hi], eg, qbt, ebt)
+        assert np.array_equal(part, full[lo:hi]), (lo, hi)
+    say("gemm_e8m0 K=0")
+    c = fp8bs.gemm_e8m0_nt(torch.zeros((5, 0), dtype=torch.uint8, device="cuda"),
+                           torch.zeros((1, 0), dtype=torch.uint8, device="cuda"),
+                           torch.zeros((64, 0), dtype=torch.uint8, device="cuda"),
+                           torch.zeros((2, 0), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert c.shape == (5, 64) and torch.count_nonzero(c.float()) == 0
+
+
+@pytest.mark.parametrize("p", [-9, 5])
+def test_gemm_e8m0_exponent_shift_scales_exactly(p):
+    """Every exponent byte of A moved by p: C is multiplied by exactly 2^p (the
+    instruction applies scales exactly; its truncation pattern is unchanged)."""
+    qa, ea, qbt, ebt = _operands(8300, 96, 256, 512)
+    say(f"gemm_e8m0 exponent shift {p}")
+    c1 = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    c2 = gpu_gemm_e8m0(qa, (ea.astype(np.int64) + p).astype(np.uint8), qbt, ebt)
+    assert np.array_equal(bits_to_f64(c2), np.ldexp(bits_to_f64(c1), p))
+
+
+def test_gemm_e8m0_exact_when_products_share_a_narrow_range():
+    """Codes from {+-0.5, +-1, +-1.5, +-2} with exponents spread by up to 2^8
+    between blocks: every product of a 128-deep step keeps all its bits in the
+    instruction's window, so C is within the bf16 rounding (half an ulp,
+    2^-8 relative) plus fp32 accumulation (2^-22 of the magnitude sum) of the
+    fp64 reference, the exact recipe's precision.  Any slip in the operand
+    layout or the scale-to-K-block mapping would miss by far more."""
+    g = np.random.default_rng(8400)
+    M, N, K = 160, 256, 1024
+    small = np.array([0x30, 0x38, 0x3C, 0x40, 0xB0, 0xB8, 0xBC, 0xC0], np.uint8)
+    qa, qbt = small[g.integers(0, 8, (M, K))], small[g.integers(0, 8, (N, K))]
+    for span in (0, 2, 8):
+        ea = (127 + g.integers(-span, span + 1, (M // 32, K // 32))).astype(np.uint8)
+        ebt = (127 + g.integers(-span, span + 1, (N // 32, K // 32))).astype(np.uint8)
+        say(f"gemm_e8m0 narrow-range codes, exponent span {span}")
+        c = bits_to_f64(gpu_gemm_e8m0(qa, ea, qbt, ebt))
+        ref, absref = oracle.gemm_ref_e8m0_nt(qa, ea, qbt, ebt)
+        assert np.all(np.abs(c - ref) <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -22 * absref), span
