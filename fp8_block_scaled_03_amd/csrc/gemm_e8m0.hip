@@ -19,7 +19,7 @@
 //
 // Tile: 128 x 128 per 256-thread workgroup; four waves of 64 x 64 (4 x 4
 // sub-tiles).  A and Bt are streamed as E4M3 bytes with direct global->LDS
-// loads into a three-stage ring of 128-deep K steps; row r of a stage holds its
+// loads into a ring of 128-deep K steps (two or three slots); row r of a stage holds its
 // 128 bytes with 16-byte piece p at position p ^ (r & 7).  Each stage also
 // carries the step's scale bytes (four K-blocks for the tile's four A
 // row-blocks and four Bt row-blocks).
@@ -29,12 +29,17 @@ namespace fp8bs {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
-constexpr int EBM = 128, EBN = 128, EBK = 128, ETHREADS = 256, ESTAGES = 3;
+constexpr int EBM = 128, EBN = 128, EBK = 128, ETHREADS = 256;
 constexpr int E_OPND_BYTES = EBM * EBK;           // 16 KB per operand and stage
 constexpr int E_SC_OFF = 2 * E_OPND_BYTES;        // scale records after A and Bt
 constexpr int E_STAGE = E_SC_OFF + 4 * 256;       // one 256-byte record per wave
-constexpr int E_LDS = ESTAGES * E_STAGE;          // 99 KB
+// Ring depth: 2 slots (67.6 KB, two workgroups per CU) when the grid has at
+// least two tiles per CU, else 3 slots (99 KB, more steps in flight for the
+// few workgroups of a decode-sized launch).  The per-element instruction
+// sequence is the same at either depth, so results do not change with M.
+constexpr int E_MANY_TILES = 512;
 
+template <int ESTAGES>
 __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* __restrict__ a,
                                                                 const uint8_t* __restrict__ ea,
                                                                 const uint8_t* __restrict__ bt,
@@ -78,7 +83,8 @@ __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* _
 
   auto issue = [&](int step) __attribute__((always_inline)) {
     // the slot follows the step; past the end the last step's bytes are
-    // reloaded into a slot that is never read again
+    // reloaded into a slot that is never read again (step ks + ESTAGES - 1
+    // lands in step ks - 1's slot)
     const uint32_t slot = ring + (step % ESTAGES) * E_STAGE;
     const int ks = step < KS ? step : KS - 1;
 #pragma unroll
@@ -101,15 +107,15 @@ __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* _
     return v8i_t{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
   };
 
-  // ring: steps ks and ks+1 in flight before step ks is consumed (9 loads per step and wave)
+  // ring of ESTAGES slots, ESTAGES - 1 steps in flight; a wave issues 9 loads per step
   if (KS > 0) {
-    issue(0);
-    issue(1);
+#pragma unroll
+    for (int s = 0; s < ESTAGES - 1; ++s) issue(s);
   }
   for (int ks = 0; ks < KS; ++ks) {
-    wait_vmcnt<9>();   // step ks has landed (step ks+1 may still be in flight)
-    lds_barrier();     // ... for every wave; step ks-1's slot is free
-    issue(ks + 2);
+    wait_vmcnt<9 * (ESTAGES - 2)>();  // step ks has landed (the later ones may still be in flight)
+    lds_barrier();                    // ... for every wave; step ks-1's slot is free
+    issue(ks + ESTAGES - 1);
     const unsigned char* slot = smem + (ks % ESTAGES) * E_STAGE;
     const unsigned char* rec = slot + E_SC_OFF + w * 256;
     v8i_t af[4], bf[4];
@@ -150,15 +156,23 @@ __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* _
 }
 
 hipError_t set_gemm_e8m0_attributes() {
-  return hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, E_LDS);
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     2 * E_STAGE);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             3 * E_STAGE);
 }
 
 hipError_t launch_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream) {
   const int64_t tiles_m = (M + EBM - 1) / EBM, tiles_n = (N + EBN - 1) / EBN;
-  hipLaunchKernelGGL(gemm_e8m0_nt_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(ETHREADS), E_LDS, stream,
-                     (const uint8_t*)a, (const uint8_t*)ea, (const uint8_t*)bt, (const uint8_t*)ebt, (uint16_t*)c,
-                     M, N, K, tiles_n);
+  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  if (tiles_m * tiles_n >= E_MANY_TILES)
+    hipLaunchKernelGGL(gemm_e8m0_nt_kernel<2>, grid, dim3(ETHREADS), 2 * E_STAGE, stream, (const uint8_t*)a,
+                       (const uint8_t*)ea, (const uint8_t*)bt, (const uint8_t*)ebt, (uint16_t*)c, M, N, K, tiles_n);
+  else
+    hipLaunchKernelGGL(gemm_e8m0_nt_kernel<3>, grid, dim3(ETHREADS), 3 * E_STAGE, stream, (const uint8_t*)a,
+                       (const uint8_t*)ea, (const uint8_t*)bt, (const uint8_t*)ebt, (uint16_t*)c, M, N, K, tiles_n);
   return hipGetLastError();
 }
 

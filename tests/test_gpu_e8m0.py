@@ -140,3 +140,13 @@ def test_gemm_e8m0_exact_when_products_share_a_narrow_range():
         c = bits_to_f64(gpu_gemm_e8m0(qa, ea, qbt, ebt))
         ref, absref = oracle.gemm_ref_e8m0_nt(qa, ea, qbt, ebt)
         assert np.all(np.abs(c - ref) <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -22 * absref), span
+
+
+def test_gemm_e8m0_ring_depth_switch_keeps_rows():
+    """2048 x 4096 runs the two-slot ring (>= 512 tiles), its first 128 rows
+    alone the three-slot ring: the rows are bitwise equal."""
+    qa, ea, qbt, ebt = _operands(8500, 2048, 4096, 256)
+    say("gemm_e8m0 ring-depth switch")
+    full = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    part = gpu_gemm_e8m0(qa[:128], ea[:4], qbt, ebt)
+    assert np.array_equal(part, full[:128])
