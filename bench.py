@@ -17,6 +17,8 @@ Also measured (same run, reported under "detail"):
     GEMM and the decode sweep in both weight layouts;
   * the fused residual add + RMSNorm + token-group quantizer at d = 8192
     (8192 rows, and 1 / 8 / 64 rows);
+  * power-of-two (E8M0) block scales, weight K-major: quantizer, the square
+    and prefill GEMMs, decode M = 8 / 64;
   * the CPU oracle on a bounded sample of the same workload ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
@@ -163,6 +165,21 @@ def main():
             flush()
             fp8bs.rmsnorm_quantize_tg(nx, ng, nwl.eps, residual=nr)
         del nx, nr, ng
+        # power-of-two (E8M0) scales: quantizer and GEMM on the square workload
+        # (weight K-major), and decode M = 8 at N = 8192
+        eqa, eea = fp8bs.quantize_e8m0(a)
+        eqb, eeb = fp8bs.quantize_e8m0(to_dev_bf16(np.ascontiguousarray(wl.b_bits().T)))
+        dwl = W.decode(8, 8192)
+        dqa, dea = fp8bs.quantize_e8m0(to_dev_bf16(dwl.a_bits()))
+        dqw, dew = fp8bs.quantize_e8m0(to_dev_bf16(np.ascontiguousarray(dwl.b_bits().T)))
+        for _ in range(3):
+            flush()
+            fp8bs.quantize_e8m0(a, eqa, eea)
+            flush()
+            fp8bs.gemm_e8m0_nt(eqa, eea, eqb, eeb, out=c)
+            flush()
+            fp8bs.gemm_e8m0_nt(dqa, dea, dqw, dew)
+        del eqa, eea, eqb, eeb, dqa, dea, dqw, dew
         # plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
         dst = torch.empty_like(src)
@@ -318,6 +335,55 @@ def main():
                                                    "tflops": round(gwl.flops() / (g_med2 * 1e-3) / 1e12, 1),
                                                    "live_groups": live}
         del gqa, gsa, gqb2, gsb2, gc
+
+        # power-of-two (E8M0) block scales on the hardware-scaled MFMA, weight
+        # K-major: quantizer, the square and prefill GEMMs, decode M = 8 / 64
+        e8 = {}
+        bt_sq = np.ascontiguousarray(wl.b_bits().T)
+        eqa, eea = fp8bs.quantize_e8m0(a)
+        eqb, eeb = fp8bs.quantize_e8m0(to_dev_bf16(bt_sq))
+        del bt_sq
+        eq_med, _, _ = time_launch(lambda: fp8bs.quantize_e8m0(a, eqa, eea), reps)
+        e8["quantize_e8m0_4096x4096_ms_median"] = round(eq_med, 5)
+        e8["quantize_e8m0_4096x4096_gbs"] = round((3 * M * K + (M // 32) * (K // 32)) / (eq_med * 1e-3) / 1e9, 1)
+        efn = lambda: fp8bs.gemm_e8m0_nt(eqa, eea, eqb, eeb, out=c)
+        for _ in range(3):
+            efn()
+        e_med, _, _ = time_launch(efn, reps)
+        e8["gemm_e8m0_4096_ms_median"] = round(e_med, 5)
+        e8["gemm_e8m0_4096_tflops_median"] = round(gemm_flops / (e_med * 1e-3) / 1e12, 1)
+        del eqa, eea, eqb, eeb
+        pwl = W.prefill(28672)
+        pqa, pea = fp8bs.quantize_e8m0(to_dev_bf16(pwl.a_bits()))
+        pqb, peb = fp8bs.quantize_e8m0(to_dev_bf16(np.ascontiguousarray(pwl.b_bits().T)))
+        pc = torch.empty((pwl.M, pwl.N), dtype=torch.bfloat16, device=dev)
+        pfn = lambda: fp8bs.gemm_e8m0_nt(pqa, pea, pqb, peb, out=pc)
+        pfn()
+        pe_med, _, _ = time_launch(pfn, 10)
+        e8["prefill_M8192_K8192_N28672"] = {"median_ms": round(pe_med, 4),
+                                            "tflops": round(pwl.flops() / (pe_med * 1e-3) / 1e12, 1)}
+        del pqa, pea, pqb, peb, pc
+        e8_dec = []
+        for n_dec in (8192, 28672):
+            dwl = W.decode(64, n_dec)
+            KB = dwl.K // 32
+            q64, e64 = fp8bs.quantize_e8m0(to_dev_bf16(dwl.a_bits()))
+            dqw, dew = fp8bs.quantize_e8m0(to_dev_bf16(np.ascontiguousarray(dwl.b_bits().T)))
+            for m in (8, 64):
+                ea_rows = (m + 31) // 32
+                dqa, dea = q64[:m].contiguous(), e64[:ea_rows].contiguous()
+                dc = torch.empty((m, n_dec), dtype=torch.bfloat16, device=dev)
+                fn = (lambda dqa=dqa, dea=dea, dc=dc: fp8bs.gemm_e8m0_nt(dqa, dea, dqw, dew, out=dc))
+                for _ in range(3):
+                    fn()
+                d_med, _, _ = time_launch(fn, reps)
+                nbytes = m * dwl.K + dwl.K * n_dec + ea_rows * KB + KB * (n_dec // 32) + 2 * m * n_dec
+                e8_dec.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
+                               "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            del q64, e64, dqw, dew
+        e8["decode_k_major_weight"] = e8_dec
+        detail["e8m0"] = e8
 
     cpu = None
     if not args.no_cpu:
