@@ -155,6 +155,108 @@ __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* _
   }
 }
 
+// ---- small M (M <= 64): one wave per 16 weight rows, all K.  A decode-sized
+// grid of 128 x 128 tiles leaves most CUs idle (64 tiles at N = 8192), so here
+// each wave owns one 16-column strip of C for the MT = ceil(M/16) row tiles and
+// streams its 16 weight rows (16 KB-aligned, K-contiguous) and the A rows
+// (small, L2-resident) straight from global memory into a register ring D
+// steps deep; no LDS.  The MFMA calls, their operands, scale bytes and order
+// are the tile kernel's, so every row is bitwise the tile kernel's row.
+constexpr int E_SMALLM_MAX = 64;
+constexpr int64_t E_SMALLM_WIDE_N = 16384;
+
+template <int MT, int D>
+__global__ void __launch_bounds__(64) gemm_e8m0_smallm_nt_kernel(const uint8_t* __restrict__ a,
+                                                                 const uint8_t* __restrict__ ea,
+                                                                 const uint8_t* __restrict__ bt,
+                                                                 const uint8_t* __restrict__ ebt,
+                                                                 uint16_t* __restrict__ c, int64_t M, int64_t N,
+                                                                 int64_t K) {
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, lo = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int KS = (int)(K / EBK);
+  const int64_t KB = K >> 5;
+  // lane (g, lo) holds row lo's K bytes [16g, 16g + 16) and [64 + 16g, 80 + 16g)
+  // of each 128-deep step; rows past M read row M - 1 (never stored)
+  const uint8_t* bp = bt + (n0 + lo) * K + 16 * g;
+  const uint8_t* ap[MT];
+  const uint8_t* sap[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    int64_t r = 16 * i + lo;
+    r = r < M ? r : M - 1;
+    ap[i] = a + r * K + 16 * g;
+    sap[i] = ea + (i >> 1) * KB;  // row tile i lies in 32-row block i / 2
+  }
+  // the step's four exponent bytes (K-blocks 4s .. 4s + 3) as one dword
+  const uint8_t* sbp = ebt + (n0 >> 5) * KB;
+
+  v4i bq[D][2];
+  v4i aq[D][MT][2];
+  uint32_t sbq[D], saq[D][MT];
+  auto load = [&](int d, int s) __attribute__((always_inline)) {
+    const int64_t o = (int64_t)s * EBK;
+    bq[d][0] = *reinterpret_cast<const v4i*>(bp + o);
+    bq[d][1] = *reinterpret_cast<const v4i*>(bp + o + 64);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      aq[d][i][0] = *reinterpret_cast<const v4i*>(ap[i] + o);
+      aq[d][i][1] = *reinterpret_cast<const v4i*>(ap[i] + o + 64);
+      saq[d][i] = *reinterpret_cast<const uint32_t*>(sap[i] + 4 * (int64_t)s);
+    }
+    sbq[d] = *reinterpret_cast<const uint32_t*>(sbp + 4 * (int64_t)s);
+  };
+
+  v4f acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto consume = [&](int d) __attribute__((always_inline)) {
+    const v8i_t bf = v8i_t{bq[d][0][0], bq[d][0][1], bq[d][0][2], bq[d][0][3],
+                           bq[d][1][0], bq[d][1][1], bq[d][1][2], bq[d][1][3]};
+    const int sb = (int)((sbq[d] >> (8 * g)) & 0xffu);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const v8i_t af = v8i_t{aq[d][i][0][0], aq[d][i][0][1], aq[d][i][0][2], aq[d][i][0][3],
+                             aq[d][i][1][0], aq[d][i][1][1], aq[d][i][1][2], aq[d][i][1][3]};
+      const int sa = (int)((saq[d][i] >> (8 * g)) & 0xffu);
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[i], 0, 0, 0, sb, 0, sa);
+    }
+  };
+
+  if (KS > 0) {
+    // Every slot is refilled unconditionally (steps past the end reload the
+    // last step, in bounds and never consumed), so each slot register has one
+    // definition per round and no in-flight load is ever copied or waited on
+    // early.
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(d, d < KS ? d : KS - 1);
+    const int full = KS - KS % D;
+    for (int s0 = 0; s0 < full; s0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        consume(d);
+        const int nxt = s0 + d + D;
+        load(d, nxt < KS ? nxt : KS - 1);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (full + d < KS) consume(d);
+  }
+
+  // lane holds row 16i + lo, columns n0 + 4g .. n0 + 4g + 3
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t row = 16 * i + lo;
+    if (row < M) {
+      const uint32_t w0 = bf16_rne(acc[i][0]) | (bf16_rne(acc[i][1]) << 16);
+      const uint32_t w1 = bf16_rne(acc[i][2]) | (bf16_rne(acc[i][3]) << 16);
+      *reinterpret_cast<uint2*>(c + row * N + n0 + 4 * g) = make_uint2(w0, w1);
+    }
+  }
+}
+
 hipError_t set_gemm_e8m0_attributes() {
   hipError_t e = hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      2 * E_STAGE);
@@ -165,6 +267,31 @@ hipError_t set_gemm_e8m0_attributes() {
 
 hipError_t launch_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c, int64_t M,
                                int64_t N, int64_t K, hipStream_t stream) {
+  // small M: one wave per 16-column strip.  Ring depth by shape: about
+  // 4-8 MB of weight in flight over the whole grid (deeper rings on a wide
+  // grid measured slower); M > 16 only while N / 16 waves fit the chip in
+  // one round at one wave per SIMD (the A rows are re-read from L2 per wave).
+  if (M <= 16 || (M <= E_SMALLM_MAX && N <= E_SMALLM_WIDE_N)) {
+    const dim3 sgrid((unsigned)(N / 16));
+    const int mt = (int)((M + 15) / 16);
+#define E8_SMALLM(MT, D)                                                                                          \
+  hipLaunchKernelGGL((gemm_e8m0_smallm_nt_kernel<MT, D>), sgrid, dim3(64), 0, stream, (const uint8_t*)a,              \
+                     (const uint8_t*)ea, (const uint8_t*)bt, (const uint8_t*)ebt, (uint16_t*)c, M, N, K)
+    if (mt == 1) {
+      if (N <= E_SMALLM_WIDE_N)
+        E8_SMALLM(1, 8);
+      else
+        E8_SMALLM(1, 4);
+    } else if (mt == 2) {
+      E8_SMALLM(2, 6);
+    } else if (mt == 3) {
+      E8_SMALLM(3, 4);
+    } else {
+      E8_SMALLM(4, 4);
+    }
+#undef E8_SMALLM
+    return hipGetLastError();
+  }
   const int64_t tiles_m = (M + EBM - 1) / EBM, tiles_n = (N + EBN - 1) / EBN;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
   if (tiles_m * tiles_n >= E_MANY_TILES)

@@ -150,3 +150,31 @@ def test_gemm_e8m0_ring_depth_switch_keeps_rows():
     full = gpu_gemm_e8m0(qa, ea, qbt, ebt)
     part = gpu_gemm_e8m0(qa[:128], ea[:4], qbt, ebt)
     assert np.array_equal(part, full[:128])
+
+
+@pytest.mark.parametrize("K", [128, 896, 1152, 4096])
+def test_gemm_e8m0_small_m_rows_equal_tile_rows(K):
+    """M <= 64 at this width runs the small-M kernel (a register ring of
+    128-deep steps, with K/128 below, at and past one ring's depth); its rows
+    are bitwise the tile kernel's rows of a 160-row call on the same operands."""
+    qa, ea, qbt, ebt = _operands(8600 + K, 160, 1024, K)
+    say(f"gemm_e8m0 small-M vs tile K={K}")
+    full = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    for m in (1, 5, 16, 17, 31, 32, 33, 48, 50, 64):
+        part = gpu_gemm_e8m0(qa[:m], ea[:-(-m // 32)], qbt, ebt)
+        assert np.array_equal(part, full[:m]), m
+    # a narrow weight (N = 32: two 16-column strips) and the oracle
+    part = gpu_gemm_e8m0(qa[:9], ea[:1], qbt[:32], ebt[:1])
+    ref, absref = oracle.gemm_ref_e8m0_nt(qa[:9], ea[:1], qbt[:32], ebt[:1])
+    assert e8m0_ok(part, ref, absref).all()
+
+
+def test_gemm_e8m0_small_m_wide_weight():
+    """Past 16384 columns M <= 16 keeps the small-M kernel (shallower ring) and
+    M = 17 .. 64 goes to the tile kernel: rows bitwise equal either way."""
+    qa, ea, qbt, ebt = _operands(8700, 160, 16416, 640)
+    say("gemm_e8m0 wide weight N=16416")
+    full = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    for m in (3, 16, 40):
+        part = gpu_gemm_e8m0(qa[:m], ea[:-(-m // 32)], qbt, ebt)
+        assert np.array_equal(part, full[:m]), m
