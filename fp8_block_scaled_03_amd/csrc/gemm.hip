@@ -128,10 +128,14 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   lds_u8* const st_a0 = sA + a_lds_off(a_row, 2 * a_half);
   lds_u8* const st_a1 = sA + a_lds_off(a_row, 2 * a_half + 1);
 
+  // Rows of A past the problem and columns of B past N load a clamped, valid
+  // address instead of zeros: they feed only outputs that are never stored.
+  // Unconditional loads let the compiler count them exactly, so the wait before
+  // staging covers only the K-block being staged, not the one loaded after it.
   auto load_stage = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
-    ra = a_ok ? *reinterpret_cast<const uint4*>(a_src + (int64_t)kb * 32) : make_uint4(0, 0, 0, 0);
+    ra = *reinterpret_cast<const uint4*>(a_src + (int64_t)kb * 32);
     const int64_t boff = BT ? (int64_t)kb * 32 : (int64_t)kb * 32 * N;
-    rb = b_ok ? *reinterpret_cast<const uint4*>(b_src + boff) : make_uint4(0, 0, 0, 0);
+    rb = *reinterpret_cast<const uint4*>(b_src + boff);
   };
   // `st` is the stage index (wave-uniform, 0..2)
   auto store_stage = [&](int st, uint4 ra, uint4 rb) __attribute__((always_inline)) {
@@ -283,9 +287,16 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
   if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
   if (KB > 1) { load_stage(1, ra, rb); store_stage(1, ra, rb); }
-  if (KB > 0) load_stage(KB > 2 ? 2 : KB - 1, ra, rb);
+  // The two register sets are loaded in the order the loop reloads them (A then
+  // B of the first set, then the second): the loop entry then matches the
+  // steady state, and the compiler can count the loads in flight exactly.
   uint4 ra2 = make_uint4(0, 0, 0, 0), rb2 = make_uint4(0, 0, 0, 0);
-  if (KB > 0) load_stage(KB > 3 ? 3 : KB - 1, ra2, rb2);
+  if (KB > 0) {
+    load_stage(KB > 2 ? 2 : KB - 1, ra, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(KB > 3 ? 3 : KB - 1, ra2, rb2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __syncthreads();
   v8bf af[4], bfrag[8];
   if (KB > 0) {
@@ -360,16 +371,24 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     if constexpr (TG) read_tg_scales(kb + 1 < KB ? kb + 1 : kb, sa4, sbs);
     else read_scales(kb + 1 < KB ? kb + 1 : kb, s_cur);
     // the window's direct loads have landed before the barrier publishes them
-    // (every iteration: a wait under a branch here costs the loop its registers)
-    if constexpr (TG) wait_vmcnt<0>();
+    // (every iteration: a wait under a branch here costs the loop its
+    // registers).  Only this iteration's two operand loads were issued after
+    // them, and they may stay in flight.
+    if constexpr (TG) wait_vmcnt<2>();
     __syncthreads();
     sn = sn == 2 ? 0 : sn + 1;
     sf = sf == 2 ? 0 : sf + 1;
   };
-  for (int kb = 0; kb < KB; kb += 2) {
+  // pairs of iterations, then an odd last K-block outside the loop: a
+  // conditional second iteration inside would give the loop's back edge two
+  // different orders of loads in flight, and the compiler would then wait for
+  // all of them before staging
+  int kb = 0;
+  for (; kb + 1 < KB; kb += 2) {
     iteration(kb, ra, rb);
-    if (kb + 1 < KB) iteration(kb + 1, ra2, rb2);
+    iteration(kb + 1, ra2, rb2);
   }
+  if (kb < KB) iteration(kb, ra, rb);
 
   // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
   // 16-byte coalesced global stores

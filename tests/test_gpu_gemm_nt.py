@@ -44,6 +44,12 @@ def _assert_tol(c_bits, ref, absref, label):
     (65, 64, 64),
     (9, 12288, 96), (16, 12288, 320),                   # K-blocks split over waves, 64-column slices
     (24, 96, 160), (32, 64, 288),                        # K-blocks split over waves, 17-32 rows
+    # deeper K: several rounds of the small-M rings plus ragged tails, for
+    # 1-4 row tiles, and a grid wider than 16384 columns
+    (1, 32, 32 * 31), (5, 64, 32 * 32), (16, 32, 32 * 33), (3, 96, 32 * 70),
+    (17, 32, 32 * 15), (32, 64, 32 * 16), (20, 32, 32 * 37),
+    (33, 32, 32 * 7), (48, 64, 32 * 8), (64, 32, 32 * 9), (57, 96, 32 * 25),
+    (2, 16416, 32 * 17), (30, 16416, 32 * 9), (64, 16416, 32 * 5),
 ])
 def test_gemm_nt_matches_oracle_and_kn_path(M, N, K):
     qa, sa = _quantized(4000 + M, M, K)

@@ -76,6 +76,9 @@ def test_quantize_tg_ignores_other_rows():
     (1, 64, 256), (8, 96, 320), (33, 32, 64), (64, 160, 96),    # small-M, narrow slices, ragged rounds
     (17, 12288, 96), (40, 28672, 64), (64, 24576, 64),          # small-M, wide slices
     (9, 12288, 96), (24, 96, 160), (32, 64, 288),                # K-blocks split over waves (K-major)
+    # deeper K with ragged tails, and a grid wider than 16384 columns
+    (1, 32, 32 * 33), (16, 64, 32 * 32), (31, 32, 32 * 17), (50, 96, 32 * 9),
+    (4, 16416, 32 * 17), (64, 16416, 32 * 5),
 ])
 def test_gemm_tg_matches_oracle(M, N, K, k_major):
     qa, sa_rows = oracle.quantize_token_groups(W.normal_bf16(1200 + M, 0, M, K, 1.0, 0.01))
