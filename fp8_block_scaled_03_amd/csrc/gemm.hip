@@ -65,6 +65,10 @@ __device__ __forceinline__ int b_lds_off(int k, int chunk) {
   return k * 512 + (k >> 3) * 128 + ((chunk ^ (k & 3)) << 5);
 }
 
+// A zero in device memory: the token-group scale window loads it (with a direct
+// global->LDS load, like every other entry) as sb past the last K-block.
+__device__ const float kZeroScale = 0.0f;
+
 struct TileArgs {
   const uint8_t* a;   // rows of this problem start here (global row index 0)
   const float* sa;    // [ceil(M/32), KB]
@@ -203,12 +207,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 #pragma unroll
     for (int i = 0; i < SCW / 8; ++i) {
       int kk = win * SCW + w_k0 + 8 * i;
-      kk = kk < KB ? kk : KB - 1;  // past the end: any valid block (never read)
+      kk = kk < KB ? kk : KB - 1;  // past the end: read any valid block, store 0
       va[i] = sa_src[kk];
       vb[i] = sb_src[(int64_t)kk * sb_kstride];
     }
 #pragma unroll
-    for (int i = 0; i < SCW / 8; ++i) dst[(w_k0 + 8 * i) * 64 + w_rb * 8 + w_cb] = va[i] * vb[i];
+    for (int i = 0; i < SCW / 8; ++i)
+      dst[(w_k0 + 8 * i) * 64 + w_rb * 8 + w_cb] = win * SCW + w_k0 + 8 * i < KB ? va[i] * vb[i] : 0.0f;
   };
   // this wave's blocks: rows wm*64.. (row-blocks 2wm, 2wm+1), cols wn*128.. (col-blocks 4wn..4wn+3)
   typedef float v4f_t __attribute__((ext_vector_type(4)));
@@ -247,10 +252,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       } else {
         const int j = pos - SCWT * 256, kk = j >> 3, cbl = j & 7;
         int kb = win * SCWT + kk;
-        kb = kb < KB ? kb : KB - 1;
+        const bool past = kb >= KB;  // past the last K-block: sb = 0
+        kb = past ? KB - 1 : kb;
         int64_t cb = cb_tile + cbl;
         cb = cb < NB ? cb : NB - 1;
-        src = BT ? p.sb + cb * KB + kb : p.sb + (int64_t)kb * NB + cb;
+        src = past ? &kZeroScale : BT ? p.sb + cb * KB + kb : p.sb + (int64_t)kb * NB + cb;
       }
       dma4(src, dst + i * 256);
     }
@@ -286,7 +292,9 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   }
   uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
   if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
-  if (KB > 1) { load_stage(1, ra, rb); store_stage(1, ra, rb); }
+  // stage 1 always holds finite codes (K-block 0 again when K has one block):
+  // an empty K-block after an odd last one multiplies whatever stage it reads
+  if (KB > 0) { load_stage(KB > 1 ? 1 : 0, ra, rb); store_stage(1, ra, rb); }
   // The two register sets are loaded in the order the loop reloads them (A then
   // B of the first set, then the second): the loop entry then matches the
   // steady state, and the compiler can count the loads in flight exactly.
@@ -368,8 +376,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       }
       if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (TG) read_tg_scales(kb + 1 < KB ? kb + 1 : kb, sa4, sbs);
-    else read_scales(kb + 1 < KB ? kb + 1 : kb, s_cur);
+    if constexpr (TG) read_tg_scales(kb + 1, sa4, sbs);
+    else read_scales(kb + 1, s_cur);
     // the window's direct loads have landed before the barrier publishes them
     // (every iteration: a wait under a branch here costs the loop its
     // registers).  Only this iteration's two operand loads were issued after
@@ -379,16 +387,17 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     sn = sn == 2 ? 0 : sn + 1;
     sf = sf == 2 ? 0 : sf + 1;
   };
-  // pairs of iterations, then an odd last K-block outside the loop: a
-  // conditional second iteration inside would give the loop's back edge two
-  // different orders of loads in flight, and the compiler would then wait for
-  // all of them before staging
-  int kb = 0;
-  for (; kb + 1 < KB; kb += 2) {
+  // Both iterations of the pair are unconditional: a conditional second one
+  // would give the loop's back edge two different orders of loads in flight,
+  // and the compiler would then wait for all of them before staging.  An odd
+  // last K-block is paired with an empty one (kb = KB) whose scale products
+  // are zero: fma(P, 0, acc) returns acc bit for bit, since P is finite (a
+  // partial of finite codes) and acc is never -0 (it starts at +0, and an
+  // exact cancellation rounds to +0).
+  for (int kb = 0; kb < KB; kb += 2) {
     iteration(kb, ra, rb);
     iteration(kb + 1, ra2, rb2);
   }
-  if (kb < KB) iteration(kb, ra, rb);
 
   // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
   // 16-byte coalesced global stores

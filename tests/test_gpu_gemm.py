@@ -39,6 +39,9 @@ def _assert_tol(c_bits, ref, absref, label):
     (65, 64, 64),         # just above the small-M limit
     (1, 24576, 96), (40, 24576, 64),      # small-M kernel, 128-column slices
     (64, 12288, 96), (17, 12288, 320),    # small-M kernel, 64-column slices; ragged last round
+    # tile kernel, odd numbers of K-blocks (the last one paired with an empty,
+    # zero-scale block): one, seven, and 65 (past a 64-block scale window)
+    (100, 64, 32), (130, 96, 32 * 7), (257, 64, 32 * 65),
 ])
 def test_gemm_matches_oracle(M, N, K):
     qa, sa = _quantized(2000 + M, M, K)
@@ -172,16 +175,17 @@ def test_row_blocks_permute_and_repeat():
         assert np.array_equal(gpu_gemm(qa, sa, qb, sb), c)
 
 
-def test_grouped_matches_oracle_and_single_gemm():
+@pytest.mark.parametrize("K", [128, 96, 32])   # even, odd and single K-block counts
+def test_grouped_matches_oracle_and_single_gemm(K):
     g = np.random.default_rng(31)
-    G, K, N = 6, 128, 96
+    G, N = 6, 96
     rows = np.array([64, 0, 288, 32, 0, 96])
     off = W.offsets_from_rows(rows)
     M = int(off[-1])
     qa, sa = _quantized(32, M, K)
     qb = np.stack([_quantized(40 + i, K, N, std=0.02)[0] for i in range(G)])
     sb = np.stack([_quantized(40 + i, K, N, std=0.02)[1] for i in range(G)])
-    say("grouped small")
+    say(f"grouped small K={K}")
     c = gpu_grouped(qa, sa, qb, sb, off)
     ref, absref = oracle.grouped_gemm_ref(qa, sa, qb, sb, off)
     _assert_tol(c, ref, absref, "grouped")

@@ -50,6 +50,7 @@ def _assert_tol(c_bits, ref, absref, label):
     (17, 32, 32 * 15), (32, 64, 32 * 16), (20, 32, 32 * 37),
     (33, 32, 32 * 7), (48, 64, 32 * 8), (64, 32, 32 * 9), (57, 96, 32 * 25),
     (2, 16416, 32 * 17), (30, 16416, 32 * 9), (64, 16416, 32 * 5),
+    (100, 64, 32), (130, 96, 32 * 7),                     # tile kernel, odd K-block counts
 ])
 def test_gemm_nt_matches_oracle_and_kn_path(M, N, K):
     qa, sa = _quantized(4000 + M, M, K)

@@ -79,6 +79,8 @@ def test_quantize_tg_ignores_other_rows():
     # deeper K with ragged tails, and a grid wider than 16384 columns
     (1, 32, 32 * 33), (16, 64, 32 * 32), (31, 32, 32 * 17), (50, 96, 32 * 9),
     (4, 16416, 32 * 17), (64, 16416, 32 * 5),
+    # tile kernel, odd K-block counts: one, and 17 (past a 16-block scale window)
+    (100, 64, 32), (130, 96, 32 * 17),
 ])
 def test_gemm_tg_matches_oracle(M, N, K, k_major):
     qa, sa_rows = oracle.quantize_token_groups(W.normal_bf16(1200 + M, 0, M, K, 1.0, 0.01))
