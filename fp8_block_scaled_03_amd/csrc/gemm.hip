@@ -344,10 +344,10 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 
     // 32 sub-tile partials, j outer, so that each B fragment is dead after its
     // four uses and is refilled with the next K-block's; partials pass through
-    // a ring of PDEPTH registers so PDEPTH MFMAs are in flight while the VALU
+    // a ring of PDEPTH partials so PDEPTH MFMAs are in flight while the VALU
     // promotes the oldest.  The staging of K-block kb+2 (decode + LDS stores)
-    // goes in after the first group of MFMAs.
-    constexpr int PDEPTH = 3;
+    // goes in after the fifth MFMA.
+    constexpr int PDEPTH = 6;
     v4f pr[PDEPTH];
 #pragma unroll
     for (int q = 0; q < 32 + PDEPTH; ++q) {
@@ -374,7 +374,10 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
         store_stage(sf, ra, rb);
         load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
       }
-      if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      // scheduling groups of three MFMAs: every promotion in a group reads a
+      // partial formed at least one group earlier, so the compiler never has
+      // to place an fma right behind the MFMA it depends on
+      if (q % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (TG) read_tg_scales(kb + 1, sa4, sbs);
     else read_scales(kb + 1, s_cur);
