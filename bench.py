@@ -256,6 +256,7 @@ def main():
                 "avg_ms": round(g_avg, 5)}
 
     detail = {
+        "sclk_mhz_during_gemm": sample_sclk(gemm_only, torch),
         "gemm_kernel_ms": {"median": round(g_med, 5), "min": round(g_min, 5), "mean": round(g_avg, 5)},
         "gemm_kernel_tflops_median": round(gemm_flops / (g_med * 1e-3) / 1e12, 1),
         "gemm_frac_of_bf16_mfma_peak": round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
@@ -454,6 +455,47 @@ def main():
         "detail": detail,
     }
     print(json.dumps(out), flush=True)
+
+
+def sample_sclk(fn, torch, seconds=1.0):
+    """Shader clock while `fn` runs back to back for about `seconds`: median of
+    the current level read from the driver's sysfs clock table every 20 ms
+    (after the first 0.3 s), or None where that file does not exist."""
+    import glob
+    import threading
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not files:
+        return None
+    samples, stop = [], threading.Event()
+
+    def read_current():
+        for line in open(files[0]).read().splitlines():
+            if line.rstrip().endswith("*"):
+                return int(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        return None
+
+    def sampler():
+        t_start = time.perf_counter()
+        while not stop.is_set():
+            v = read_current()
+            if v is not None and time.perf_counter() - t_start > 0.3:
+                samples.append(v)
+            time.sleep(0.02)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    samples.sort()
+    return {"median": samples[len(samples) // 2], "min": samples[0], "max": samples[-1], "samples": len(samples),
+            "source": files[0]}
 
 
 def cpu_baseline(wl):
