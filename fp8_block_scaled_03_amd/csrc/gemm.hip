@@ -234,7 +234,8 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // read.
   // Filled with direct global->LDS dword loads (no registers): dword d of the
   // window is loaded by lane d % 64 of load d / 64, and waited for with an
-  // explicit vmcnt(0) before the barrier that ends the iteration.
+  // explicit vmcnt count before the barrier that ends the iteration (only
+  // that iteration's two operand loads may still be in flight).
   const uint32_t sc_lds_addr = (uint32_t)(uintptr_t)((lds_u8*)sc_lds);
   auto load_tg_window = [&](int win) __attribute__((always_inline)) {
     const uint32_t dst = sc_lds_addr + (win & 1) * TG_WINDOW_BYTES;
