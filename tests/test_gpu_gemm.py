@@ -42,6 +42,9 @@ def _assert_tol(c_bits, ref, absref, label):
     # tile kernel, odd numbers of K-blocks (the last one paired with an empty,
     # zero-scale block): one, seven, and 65 (past a 64-block scale window)
     (100, 64, 32), (130, 96, 32 * 7), (257, 64, 32 * 65),
+    # small-M kernel, 128-column slices, 17-32 rows: A decoded once per
+    # workgroup into a shared bf16 area (several rounds, a ragged last round)
+    (17, 24576, 32 * 9), (32, 24576, 32 * 17), (24, 24576, 64),
 ])
 def test_gemm_matches_oracle(M, N, K):
     qa, sa = _quantized(2000 + M, M, K)
@@ -151,7 +154,7 @@ def test_rows_independent_of_batch_wide_slices(N):
     full = gpu_gemm(qa, sa, qb, sb)
     ref, absref = oracle.gemm_ref(qa, sa, qb, sb)
     _assert_tol(full, ref, absref, f"wide M=320 N={N}")
-    for m in (64, 33, 8, 1):
+    for m in (64, 33, 32, 20, 8, 1):
         say(f"wide invariance prefix M={m} N={N}")
         pre = gpu_gemm(qa[:m], sa[:-(-m // 32)], qb, sb)
         assert np.array_equal(pre, full[:m]), f"M={m}"
