@@ -824,13 +824,20 @@ struct SmallMNtCfg {
   static constexpr int SC_OFF = A_OFF + 32 * ACH * 256;
   static constexpr int REC = TG ? 512 : 256;  // scale record per K-block (token groups: sa rows, then sb)
   static constexpr int SLOT = SC_OFF + SWAVES * REC;
-  static constexpr int D_FIT = SMALL_LDS_BUDGET / SLOT;
-  static constexpr int D = D_FIT > 6 ? 6 : D_FIT;
-  static constexpr int LDS = D * SLOT;
   static constexpr int OPS = NCB + ACH + (TG ? 2 : 1);
   static constexpr int CS = 2 * NCB;
   static constexpr int RG = SWAVES / CS;
   static constexpr int TPW = (MT + RG - 1) / RG;
+  // Shared bf16 A, as in the [K, N] kernel: where a wave owns two or more row
+  // tiles of one A chunk, each wave decodes the four A rows it loaded into a
+  // double-buffered bf16 area [2 rounds][32 rows][8 K-blocks x 64 B].
+  static constexpr int ABUF_FULL = 2 * 32 * SWAVES * 64;
+  static constexpr bool A_SHARED = ACH == 1 && TPW >= 2 && (SMALL_LDS_BUDGET - ABUF_FULL) / SLOT >= 3;
+  static constexpr int ABUF_BYTES = A_SHARED ? ABUF_FULL : 0;
+  static constexpr int D_FIT = (SMALL_LDS_BUDGET - ABUF_BYTES) / SLOT;
+  static constexpr int D = D_FIT > 6 ? 6 : D_FIT;
+  static constexpr int ABUF_OFF = D * SLOT;
+  static constexpr int LDS = ABUF_OFF + ABUF_BYTES;
   static_assert(D >= 3, "ring too shallow");
   static_assert(LDS <= SMALL_LDS_BUDGET, "LDS budget");
   static_assert((D - 2) * OPS < 64, "vmcnt range");
@@ -936,18 +943,44 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
     return row * 256 + 16 * ((2 * q + fr_hi) ^ (lane & 15)) + fr_half;
   };
 
-  auto compute = [&](int slot, int nkb, auto FULL_) __attribute__((always_inline)) {
+  // Shared bf16 A: row R's 16-byte bf16 piece p (K-block p >> 2, K elements
+  // 8*(p & 3) ..) sits at position p ^ (R & 15) of the row's 512 bytes.  Wave w
+  // decodes its own rows 4w .. 4w + 3 (lane l: row 4w + (l >> 4), the raw piece
+  // at position l & 15, i.e. global piece (l & 15) ^ (R & 15)) after its loads
+  // have landed and before the round's barrier; rows past M are not loaded
+  // and not decoded (they only reach outputs that are never stored).
+  auto decode_own_a = [&](int r) __attribute__((always_inline)) {
+    if (a_live == 0) return;
+    const int R = 4 * w + (lane >> 4);
+    const int g = (lane & 15) ^ (R & 15);
+    const unsigned char* src = smem + (r % D) * Cfg::SLOT + Cfg::A_OFF + w * 1024 + lane * 16;
+    uint4 lo, hi;
+    e4m3x16_to_bf16x16(*reinterpret_cast<const uint4*>(src), lo, hi);
+    unsigned char* dst = smem + Cfg::ABUF_OFF + (r & 1) * (32 * 512) + R * 512;
+    const int p0 = 4 * (g >> 1) + 2 * (g & 1);
+    *reinterpret_cast<uint4*>(dst + ((p0 ^ (R & 15)) << 4)) = lo;
+    *reinterpret_cast<uint4*>(dst + (((p0 + 1) ^ (R & 15)) << 4)) = hi;
+  };
+  auto compute = [&](int r, int nkb, auto FULL_) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(FULL_)::value;
-    const unsigned char* sl = smem + slot * Cfg::SLOT;
+    const unsigned char* sl = smem + (r % D) * Cfg::SLOT;
     v2i braw[SWAVES];
     v2i araw[SWAVES][Cfg::TPW];
+    v8bf abf[SWAVES][Cfg::TPW];
     float sbv[SWAVES], sav[SWAVES][2], sat[SWAVES][Cfg::TPW];
 #pragma unroll
     for (int q = 0; q < SWAVES; ++q) {
       braw[q] = *reinterpret_cast<const v2i*>(sl + frag_off(16 * cs + (lane & 15), q));
 #pragma unroll
-      for (int t = 0; t < Cfg::TPW; ++t)
-        araw[q][t] = *reinterpret_cast<const v2i*>(sl + Cfg::A_OFF + frag_off(16 * tile_of(t) + (lane & 15), q));
+      for (int t = 0; t < Cfg::TPW; ++t) {
+        if constexpr (Cfg::A_SHARED) {
+          const int row = 16 * tile_of(t) + (lane & 15);
+          const unsigned char* ab = smem + Cfg::ABUF_OFF + (r & 1) * (32 * 512) + row * 512;
+          abf[q][t] = *reinterpret_cast<const v8bf*>(ab + (((4 * q + (lane >> 4)) ^ (row & 15)) << 4));
+        } else {
+          araw[q][t] = *reinterpret_cast<const v2i*>(sl + Cfg::A_OFF + frag_off(16 * tile_of(t) + (lane & 15), q));
+        }
+      }
       const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF + q * Cfg::REC);
       if constexpr (TG) {
 #pragma unroll
@@ -964,7 +997,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
       const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
 #pragma unroll
       for (int t = 0; t < Cfg::TPW; ++t) {
-        const v8bf afrag = e4m3x8_to_bf16x8(araw[q][t]);
+        const v8bf afrag = Cfg::A_SHARED ? abf[q][t] : e4m3x8_to_bf16x8(araw[q][t]);
         const v4f p = TG ? mfma_partial(bfrag, afrag) : mfma_partial(afrag, bfrag);
         const float sc = (TG ? sat[q][t] : sav[q][tile_of(t) >> 1]) * sbv[q];
         if (FULL || q < nkb) promote(acc[t], p, sc);
@@ -984,11 +1017,14 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
     if (a_live == 0) wait_vmcnt<LB>();
     else if (a_live == 1) wait_vmcnt<LB + (D - 2)>();
     else wait_vmcnt<LB + 2 * (D - 2)>();
+    // the shared A area of round r - 2 is free: every wave finished that
+    // round's compute before the previous barrier
+    if constexpr (Cfg::A_SHARED) decode_own_a(r);
     lds_barrier();                     // ... and everyone else's; round r-1's slot is free
     issue(r + D - 1);                  // refill the slot that round r-1 used
     if (owns) {
-      if (r < full_rounds) compute(r % D, SWAVES, std::true_type{});
-      else compute(r % D, KB - r * SWAVES, std::false_type{});
+      if (r < full_rounds) compute(r, SWAVES, std::true_type{});
+      else compute(r, KB - r * SWAVES, std::false_type{});
     }
   }
   wait_vmcnt<0>();

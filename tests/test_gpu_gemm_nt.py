@@ -51,6 +51,9 @@ def _assert_tol(c_bits, ref, absref, label):
     (33, 32, 32 * 7), (48, 64, 32 * 8), (64, 32, 32 * 9), (57, 96, 32 * 25),
     (2, 16416, 32 * 17), (30, 16416, 32 * 9), (64, 16416, 32 * 5),
     (100, 64, 32), (130, 96, 32 * 7),                     # tile kernel, odd K-block counts
+    # 128-column slices, 17-32 rows: A decoded once per workgroup into a
+    # shared bf16 area (several rounds, ragged last rounds)
+    (17, 32768, 32 * 9), (32, 28672, 32 * 17), (24, 28672, 64),
 ])
 def test_gemm_nt_matches_oracle_and_kn_path(M, N, K):
     qa, sa = _quantized(4000 + M, M, K)
@@ -75,6 +78,18 @@ def test_gemm_nt_rows_independent_of_batch():
     for i in (3, 200):
         say(f"nt invariance row {i}")
         assert np.array_equal(gpu_gemm_nt(qa[i:i + 1], sa[i // 32:i // 32 + 1], qbt, sbt)[0], full[i])
+
+
+def test_gemm_nt_rows_independent_of_batch_wide_slices():
+    """128-column K-major slices (N = 28672): prefixes of 17-32 rows (A decoded
+    once per workgroup) and of 1-16 and 33-64 rows give the tile kernel's bits."""
+    qa, sa = _quantized(63, 320, 32 * 11)
+    qbt, sbt = _quantized(64, 28672, 32 * 11, std=0.02)
+    say("nt wide invariance full M=320")
+    full = gpu_gemm_nt(qa, sa, qbt, sbt)
+    for m in (64, 40, 32, 20, 17, 16, 1):
+        say(f"nt wide invariance prefix M={m}")
+        assert np.array_equal(gpu_gemm_nt(qa[:m], sa[:-(-m // 32)], qbt, sbt), full[:m]), f"M={m}"
 
 
 def test_gemm_nt_empty_k():
