@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--reps", type=int, default=50, help="per-kernel timed launches (flushed)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--quick", action="store_true", help="fewer reps, no decode sweep (for profiling)")
+    p.add_argument("--no-sclk", action="store_true",
+                   help="skip the one-second shader-clock sample (for profiler runs: its back-to-back GEMMs "
+                        "would dominate the kernel statistics)")
     p.add_argument("--profile-kernels", action="store_true",
                    help="run each kernel a few times without timing (for rocprofv3 counter passes)")
     return p.parse_args()
@@ -256,7 +259,7 @@ def main():
                 "avg_ms": round(g_avg, 5)}
 
     detail = {
-        "sclk_mhz_during_gemm": sample_sclk(gemm_only, torch),
+        "sclk_mhz_during_gemm": None if args.no_sclk else sample_sclk(gemm_only, torch),
         "gemm_kernel_ms": {"median": round(g_med, 5), "min": round(g_min, 5), "mean": round(g_avg, 5)},
         "gemm_kernel_tflops_median": round(gemm_flops / (g_med * 1e-3) / 1e12, 1),
         "gemm_frac_of_bf16_mfma_peak": round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
