@@ -460,6 +460,19 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def current_sclk_mhz(table: str):
+    """The level marked current ('*') in the driver's shader-clock table, in
+    MHz (lines like '1: 2309Mhz *'; 'S: 95Mhz *' is the deep-sleep level), or
+    None when no line is marked."""
+    for line in table.splitlines():
+        line = line.strip()
+        if line.endswith("*") and ":" in line:
+            value = line.split(":", 1)[1].rstrip("*").strip().lower()
+            if value.endswith("mhz") and value[:-3].strip().isdigit():
+                return int(value[:-3])
+    return None
+
+
 def sample_sclk(fn, torch, seconds=1.0):
     """Shader clock while `fn` runs back to back for about `seconds`: median of
     the current level read from the driver's sysfs clock table every 20 ms
@@ -472,10 +485,8 @@ def sample_sclk(fn, torch, seconds=1.0):
     samples, stop = [], threading.Event()
 
     def read_current():
-        for line in open(files[0]).read().splitlines():
-            if line.rstrip().endswith("*"):
-                return int(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
-        return None
+        with open(files[0]) as f:
+            return current_sclk_mhz(f.read())
 
     def sampler():
         t_start = time.perf_counter()
