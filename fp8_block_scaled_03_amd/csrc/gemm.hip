@@ -96,7 +96,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = wave_id_uniform();
-  const int wm = w & 3, wn = w >> 2;
+  // Waves are dealt to the four SIMDs round-robin (wave w on SIMD w % 4), so
+  // row band wm = w >> 1 gives every SIMD one wave in the tile's upper half
+  // and one in its lower half: in a tile whose last rows lie past the
+  // problem, the waves of bands with no rows skip their MFMAs and promotions
+  // and every SIMD keeps one busy wave.
+  const int wm = w >> 1, wn = w & 1;
   const int64_t K = p.K, N = p.N;
   const int KB = (int)(K >> 5);
   const int NB = (int)(N >> 5);
@@ -334,7 +339,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // Two register sets alternate between iterations: the global loads of a
   // K-block are issued two iterations before its staging, so their latency
   // hides behind two iterations of MFMAs.
-  auto iteration = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
+  // `compute_tag` (std::true_type / std::false_type): false for a wave whose
+  // row band holds no rows of the problem; it then only stages, refills the
+  // scale windows and meets the barriers.
+  auto iteration = [&](int kb, uint4& ra, uint4& rb, auto compute_tag) __attribute__((always_inline)) {
+    constexpr bool COMPUTE = decltype(compute_tag)::value;
     // next window of scales: written now, first read SCW (SCWT) iterations later
     const bool tg_refill = TG && kb % SCWT == 0 && kb + SCWT < KB;
     if constexpr (TG) {
@@ -350,8 +359,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     // goes in after the fifth MFMA.
     constexpr int PDEPTH = 6;
     v4f pr[PDEPTH];
+    if constexpr (!COMPUTE) {
+      store_stage(sf, ra, rb);
+      load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
+    }
 #pragma unroll
-    for (int q = 0; q < 32 + PDEPTH; ++q) {
+    for (int q = 0; q < (COMPUTE ? 32 + PDEPTH : 0); ++q) {
       if (q >= PDEPTH) {
         const int u = q - PDEPTH;
         const int ui = u & 3, uj = u >> 2;
@@ -380,8 +393,10 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       // to place an fma right behind the MFMA it depends on
       if (q % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (TG) read_tg_scales(kb + 1, sa4, sbs);
-    else read_scales(kb + 1, s_cur);
+    if constexpr (COMPUTE) {
+      if constexpr (TG) read_tg_scales(kb + 1, sa4, sbs);
+      else read_scales(kb + 1, s_cur);
+    }
     // the window's direct loads have landed before the barrier publishes them
     // (every iteration: a wait under a branch here costs the loop its
     // registers).  Only this iteration's two operand loads were issued after
@@ -398,9 +413,16 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // are zero: fma(P, 0, acc) returns acc bit for bit, since P is finite (a
   // partial of finite codes) and acc is never -0 (it starts at +0, and an
   // exact cancellation rounds to +0).
-  for (int kb = 0; kb < KB; kb += 2) {
-    iteration(kb, ra, rb);
-    iteration(kb + 1, ra2, rb2);
+  if (p.row0 + wm * 64 < p.row_end) {
+    for (int kb = 0; kb < KB; kb += 2) {
+      iteration(kb, ra, rb, std::true_type{});
+      iteration(kb + 1, ra2, rb2, std::true_type{});
+    }
+  } else {
+    for (int kb = 0; kb < KB; kb += 2) {
+      iteration(kb, ra, rb, std::false_type{});
+      iteration(kb + 1, ra2, rb2, std::false_type{});
+    }
   }
 
   // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
