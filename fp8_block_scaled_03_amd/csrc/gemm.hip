@@ -20,14 +20,17 @@
 //    overlapping the next tile's loads with compute).  A fragments are read
 //    K-contiguous with ds_read_b128; B is N-contiguous in memory, so its
 //    fragments come from the LDS transpose read ds_read_b64_tr_b16 (a K-major
-//    weight is staged like A instead).
+//    weight is staged like A instead).  Waves whose 64-row band lies wholly
+//    past the problem's rows only stage and meet the barriers.
 //  * small-M kernels (M <= 64, decode): a workgroup owns a slice of 32, 64 or
 //    128 columns of C for all rows and all of K and streams its slice of the
 //    weight once, eight K-blocks per round, with direct global->LDS loads into
 //    a ring several rounds deep.  Waves own whole 16x16 output sub-tiles and
-//    run their promotion chains in ascending K-block order; for one-tile
-//    slices of a K-major weight the split kernel instead forms each K-block's
-//    partials on a different wave and promotes them in order one round later.
+//    run their promotion chains in ascending K-block order (with 17-32 rows
+//    on 128-column slices A is decoded once per workgroup into a shared bf16
+//    area); for one-tile slices of a K-major weight the split kernel instead
+//    forms each K-block's partials on a different wave and promotes them in
+//    order one round later.
 #include "common.hpp"
 
 #include <type_traits>
