@@ -598,8 +598,11 @@ struct SmallMCfg {
   static constexpr int SC_OFF = B_BYTES + ACH * 1024;  // scale record(s) after B and A
   // block scales: one 256-byte record (sa of 2 row-blocks, sb); token-group
   // scales: sa of every row (256 bytes), then sb (256 bytes)
-  static constexpr int SLOT = SC_OFF + (TG ? 512 : 256);
-  static constexpr int OPS = NCB + ACH + (TG ? 2 : 1);  // direct loads per K-block
+  // token-group scales with at most 32 rows: one packed record (lanes 0-31 sa
+  // of rows 0-31, lanes 32.. sb of the column blocks)
+  static constexpr bool TG_PACKED = TG && MT <= 2;
+  static constexpr int SLOT = SC_OFF + (TG && !TG_PACKED ? 512 : 256);
+  static constexpr int OPS = NCB + ACH + (TG && !TG_PACKED ? 2 : 1);  // direct loads per K-block
   static constexpr int CS = 2 * NCB;                   // 16-column sub-tiles per workgroup
   static constexpr int RG = SWAVES / CS;               // row-tile groups
   static constexpr int TPW = (MT + RG - 1) / RG;       // row tiles per wave (at most)
@@ -678,6 +681,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
   // lane l = sb of column block cb0 + min(l, NCB-1)
   const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
   const float* const tg_sb_src = sb + cb0 + (lane < NCB ? lane : NCB - 1);
+  // packed record (M <= 32): lane l < 32 = sa of row min(l, M-1), lane 32 + j =
+  // sb of column block cb0 + min(j, NCB-1); sa steps 1, sb steps NB per K-block
+  const float* const tg_pk_src = lane < 32 ? sa + (int64_t)(lane < M ? lane : M - 1) * KB
+                                           : sb + cb0 + (lane - 32 < NCB ? lane - 32 : NCB - 1);
+  const int64_t tg_pk_stride = lane < 32 ? 1 : NB;
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   const uint32_t ring_w = (uint32_t)(uintptr_t)((lds_u8*)(smem + w * D * Cfg::SLOT));
 
@@ -689,7 +697,9 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
     for (int i = 0; i < NCB; ++i) dma16(b_src[i] + (int64_t)kc * 32 * N, sl + i * 1024);
 #pragma unroll
     for (int ch = 0; ch < Cfg::ACH; ++ch) dma16(a_src[ch] + (int64_t)kc * 32, sl + Cfg::B_BYTES + ch * 1024);
-    if constexpr (TG) {
+    if constexpr (Cfg::TG_PACKED) {
+      dma4(tg_pk_src + (int64_t)kc * tg_pk_stride, sl + Cfg::SC_OFF);
+    } else if constexpr (TG) {
       dma4(tg_sa_src + kc, sl + Cfg::SC_OFF);
       dma4(tg_sb_src + (int64_t)kc * NB, sl + Cfg::SC_OFF + 256);
     } else {
@@ -762,7 +772,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
         // this lane's row scale in each owned row tile (rows 16*i + (lane&15))
 #pragma unroll
         for (int t = 0; t < Cfg::TPW; ++t) sat[q][t] = scr[16 * tile_of(t) + (lane & 15)];
-        sbv[q] = scr[64 + own_cb];
+        sbv[q] = scr[(Cfg::TG_PACKED ? 32 : 64) + own_cb];
       } else {
         sav[q][0] = scr[0];
         sav[q][1] = scr[1];
@@ -847,9 +857,12 @@ struct SmallMNtCfg {
   static constexpr int ACH = (MT + 1) / 2;
   static constexpr int A_OFF = W * 256;
   static constexpr int SC_OFF = A_OFF + 32 * ACH * 256;
-  static constexpr int REC = TG ? 512 : 256;  // scale record per K-block (token groups: sa rows, then sb)
+  // token-group scales with at most 32 rows: one packed record, as in the
+  // [K, N] kernel
+  static constexpr bool TG_PACKED = TG && MT <= 2;
+  static constexpr int REC = TG && !TG_PACKED ? 512 : 256;  // scale record per K-block (token groups: sa rows, then sb)
   static constexpr int SLOT = SC_OFF + SWAVES * REC;
-  static constexpr int OPS = NCB + ACH + (TG ? 2 : 1);
+  static constexpr int OPS = NCB + ACH + (TG && !TG_PACKED ? 2 : 1);
   static constexpr int CS = 2 * NCB;
   static constexpr int RG = SWAVES / CS;
   static constexpr int TPW = (MT + RG - 1) / RG;
@@ -921,6 +934,10 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
   // lane l = sbt of column block cb0 + min(l, NCB-1)
   const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
   const float* const tg_sb_src = sbt + (int64_t)(cb0 + (lane < NCB ? lane : NCB - 1)) * KB;
+  // packed record (M <= 32): lane l < 32 = sa of row min(l, M-1), lane 32 + j =
+  // sbt of column block cb0 + min(j, NCB-1); both step 1 per K-block
+  const float* const tg_pk_src =
+      lane < 32 ? tg_sa_src : sbt + (int64_t)(cb0 + (lane - 32 < NCB ? lane - 32 : NCB - 1)) * KB;
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
 
@@ -940,7 +957,9 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
       if (ch < a_live) dma16(a_row[ch] + koff(r, a_g[ch]), sl + Cfg::A_OFF + (w + 8 * ch) * 1024);
     int kc = r * SWAVES + w;
     kc = kc < KB ? kc : KB - 1;
-    if constexpr (TG) {
+    if constexpr (Cfg::TG_PACKED) {
+      dma4(tg_pk_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+    } else if constexpr (TG) {
       dma4(tg_sa_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
       dma4(tg_sb_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC + 256);
     } else {
@@ -1010,7 +1029,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
       if constexpr (TG) {
 #pragma unroll
         for (int t = 0; t < Cfg::TPW; ++t) sat[q][t] = scr[16 * tile_of(t) + (lane & 15)];
-        sbv[q] = scr[64 + own_cb];
+        sbv[q] = scr[(Cfg::TG_PACKED ? 32 : 64) + own_cb];
       } else {
         sav[q][0] = scr[0];
         sav[q][1] = scr[1];
@@ -1038,7 +1057,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
   }
   for (int r = 0; r < rounds; ++r) {
     // this wave's round-r loads have landed: NCB + a_live + 1 loads per round
-    constexpr int LB = (D - 2) * (NCB + (TG ? 2 : 1));
+    constexpr int LB = (D - 2) * (NCB + (TG && !Cfg::TG_PACKED ? 2 : 1));
     if (a_live == 0) wait_vmcnt<LB>();
     else if (a_live == 1) wait_vmcnt<LB + (D - 2)>();
     else wait_vmcnt<LB + 2 * (D - 2)>();

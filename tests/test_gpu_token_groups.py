@@ -81,6 +81,9 @@ def test_quantize_tg_ignores_other_rows():
     (4, 16416, 32 * 17), (64, 16416, 32 * 5),
     # tile kernel, odd K-block counts: one, and 17 (past a 16-block scale window)
     (100, 64, 32), (130, 96, 32 * 17),
+    # small-M, 128-column slices, 17-32 rows: packed scale record and A decoded
+    # once per workgroup
+    (20, 28672, 32 * 9), (32, 28672, 32 * 5),
 ])
 def test_gemm_tg_matches_oracle(M, N, K, k_major):
     qa, sa_rows = oracle.quantize_token_groups(W.normal_bf16(1200 + M, 0, M, K, 1.0, 0.01))
