@@ -602,7 +602,12 @@ struct SmallMCfg {
   // of rows 0-31, lanes 32.. sb of the column blocks)
   static constexpr bool TG_PACKED = TG && MT <= 2;
   static constexpr int SLOT = SC_OFF + (TG && !TG_PACKED ? 512 : 256);
-  static constexpr int OPS = NCB + ACH + (TG && !TG_PACKED ? 2 : 1);  // direct loads per K-block
+  // 32x32 scales: wave 0 loads the whole round's scale record (sa of up to
+  // two row-blocks and sb of the slice's column blocks for eight K-blocks)
+  // with one direct load; token-group records stay one per wave and K-block
+  static constexpr bool ROUND_SC = !TG;
+  static constexpr int OPS = NCB + ACH + (TG && !TG_PACKED ? 2 : 1);  // direct loads per K-block (wave 0)
+  static constexpr int OPS_OTHER = ROUND_SC ? NCB + ACH : OPS;        // the other waves
   static constexpr int CS = 2 * NCB;                   // 16-column sub-tiles per workgroup
   static constexpr int RG = SWAVES / CS;               // row-tile groups
   static constexpr int TPW = (MT + RG - 1) / RG;       // row tiles per wave (at most)
@@ -671,12 +676,16 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
     row = row < M ? row : M - 1;
     a_src[ch] = a + row * K + (lane & 1) * 16;
   }
-  // Scales: lanes 0, 1 load sa of row-blocks 0, 1 (clamped to the last one);
-  // lanes 2 .. 2+NCB-1 load sb of the workgroup's column blocks (the rest repeat the last).
   const int nrb = (int)((M + 31) >> 5);
-  const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
-  const float* const sc_src = lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sb + cb0 + sbj;
-  const int64_t sc_stride = lane < 2 ? 1 : NB;
+  // round record (wave 0): lane l < 16 = sa of row-block min(l >> 3, nrb-1) at
+  // K-block 8r + (l & 7); lane 16 + 8j' .. = sb of column block cb0 + c at
+  // K-block 8r + q for l - 16 = q * NCB + c (lanes past 16 + 8*NCB repeat the
+  // last entry); every address is clamped to the last K-block
+  const int rs_l = lane < 16 ? lane : (lane - 16 < 8 * NCB ? lane - 16 : 8 * NCB - 1);
+  const int rs_q = lane < 16 ? (rs_l & 7) : rs_l / NCB;
+  const float* const rs_src = lane < 16 ? sa + (int64_t)((lane >> 3) < nrb ? (lane >> 3) : nrb - 1) * KB
+                                        : sb + cb0 + rs_l % NCB;
+  const int64_t rs_stride = lane < 16 ? 1 : NB;
   // token-group scales: record 1, lane l = sa of row min(l, M-1); record 2,
   // lane l = sb of column block cb0 + min(l, NCB-1)
   const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
@@ -703,7 +712,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
       dma4(tg_sa_src + kc, sl + Cfg::SC_OFF);
       dma4(tg_sb_src + (int64_t)kc * NB, sl + Cfg::SC_OFF + 256);
     } else {
-      dma4(sc_src + kc * sc_stride, sl + Cfg::SC_OFF);
+      if (w == 0) {
+        int kr = r * SWAVES + rs_q;
+        kr = kr < KB ? kr : KB - 1;
+        dma4(rs_src + (int64_t)kr * rs_stride, sl + Cfg::SC_OFF);
+      }
     }
   };
 
@@ -774,9 +787,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
         for (int t = 0; t < Cfg::TPW; ++t) sat[q][t] = scr[16 * tile_of(t) + (lane & 15)];
         sbv[q] = scr[(Cfg::TG_PACKED ? 32 : 64) + own_cb];
       } else {
-        sav[q][0] = scr[0];
-        sav[q][1] = scr[1];
-        sbv[q] = scr[2 + own_cb];
+        // the round record in wave 0's slot
+        const float* rec = reinterpret_cast<const float*>(smem + slot * Cfg::SLOT + Cfg::SC_OFF);
+        sav[q][0] = rec[q];
+        sav[q][1] = rec[8 + q];
+        sbv[q] = rec[16 + q * NCB + own_cb];
       }
     }
 #pragma unroll
@@ -801,7 +816,9 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
   }
 
   for (int r = 0; r < rounds; ++r) {
-    wait_vmcnt<(D - 2) * Cfg::OPS>();  // this wave's round-r loads have landed
+    // this wave's round-r loads have landed
+    if (w == 0) wait_vmcnt<(D - 2) * Cfg::OPS>();
+    else wait_vmcnt<(D - 2) * Cfg::OPS_OTHER>();
     // the shared A area of round r - 2 is free: every wave finished that
     // round's compute before the previous barrier
     if constexpr (Cfg::A_SHARED) decode_own_a(r);
