@@ -880,6 +880,10 @@ struct SmallMNtCfg {
   static constexpr int REC = TG && !TG_PACKED ? 512 : 256;  // scale record per K-block (token groups: sa rows, then sb)
   static constexpr int SLOT = SC_OFF + SWAVES * REC;
   static constexpr int OPS = NCB + ACH + (TG && !TG_PACKED ? 2 : 1);
+  // 32x32 scales: wave 0 loads the whole round's scale record with one direct
+  // load (as in the [K, N] kernel); SCL = scale loads per round of the other waves
+  static constexpr bool ROUND_SC = !TG;
+  static constexpr int SCL = ROUND_SC ? 0 : (TG && !TG_PACKED ? 2 : 1);
   static constexpr int CS = 2 * NCB;
   static constexpr int RG = SWAVES / CS;
   static constexpr int TPW = (MT + RG - 1) / RG;
@@ -945,8 +949,14 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
     a_live += 4 * (w + 8 * ch) < M ? 1 : 0;
   }
   const int nrb = (int)((M + 31) >> 5);
-  const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
-  const float* const sc_src = lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sbt + (int64_t)(cb0 + sbj) * KB;
+  // round record (wave 0): lane l < 16 = sa of row-block min(l >> 3, nrb-1) at
+  // K-block 8r + (l & 7); lane 16 + q*NCB + c = sbt of column block cb0 + c at
+  // K-block 8r + q (lanes past 16 + 8*NCB repeat the last entry); both step 1
+  // per K-block, and every K-block index is clamped to the last one
+  const int rs_l = lane < 16 ? lane : (lane - 16 < 8 * NCB ? lane - 16 : 8 * NCB - 1);
+  const int rs_q = lane < 16 ? (rs_l & 7) : rs_l / NCB;
+  const float* const rs_src = lane < 16 ? sa + (int64_t)((lane >> 3) < nrb ? (lane >> 3) : nrb - 1) * KB
+                                        : sbt + (int64_t)(cb0 + rs_l % NCB) * KB;
   // token-group scales: record 1, lane l = sa of row min(l, M-1); record 2,
   // lane l = sbt of column block cb0 + min(l, NCB-1)
   const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
@@ -980,7 +990,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
       dma4(tg_sa_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
       dma4(tg_sb_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC + 256);
     } else {
-      dma4(sc_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+      if (w == 0) {
+        int kr = r * SWAVES + rs_q;
+        kr = kr < KB ? kr : KB - 1;
+        dma4(rs_src + kr, sl + Cfg::SC_OFF);
+      }
     }
   };
 
@@ -1048,9 +1062,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
         for (int t = 0; t < Cfg::TPW; ++t) sat[q][t] = scr[16 * tile_of(t) + (lane & 15)];
         sbv[q] = scr[(Cfg::TG_PACKED ? 32 : 64) + own_cb];
       } else {
-        sav[q][0] = scr[0];
-        sav[q][1] = scr[1];
-        sbv[q] = scr[2 + own_cb];
+        // the round record (wave 0's)
+        const float* rec = reinterpret_cast<const float*>(sl + Cfg::SC_OFF);
+        sav[q][0] = rec[q];
+        sav[q][1] = rec[8 + q];
+        sbv[q] = rec[16 + q * NCB + own_cb];
       }
     }
 #pragma unroll
@@ -1074,10 +1090,16 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
   }
   for (int r = 0; r < rounds; ++r) {
     // this wave's round-r loads have landed: NCB + a_live + 1 loads per round
-    constexpr int LB = (D - 2) * (NCB + (TG && !Cfg::TG_PACKED ? 2 : 1));
+    constexpr int LB = (D - 2) * (NCB + Cfg::SCL);
+    constexpr int LB0 = Cfg::ROUND_SC ? D - 2 : 0;  // wave 0's round records (wave 0 always loads A)
     if (a_live == 0) wait_vmcnt<LB>();
-    else if (a_live == 1) wait_vmcnt<LB + (D - 2)>();
-    else wait_vmcnt<LB + 2 * (D - 2)>();
+    else if (a_live == 1) {
+      if (w == 0) wait_vmcnt<LB + LB0 + (D - 2)>();
+      else wait_vmcnt<LB + (D - 2)>();
+    } else {
+      if (w == 0) wait_vmcnt<LB + LB0 + 2 * (D - 2)>();
+      else wait_vmcnt<LB + 2 * (D - 2)>();
+    }
     // the shared A area of round r - 2 is free: every wave finished that
     // round's compute before the previous barrier
     if constexpr (Cfg::A_SHARED) decode_own_a(r);
