@@ -1171,6 +1171,10 @@ struct SmallMNtSplitCfg {
   static_assert(D >= 3, "ring too shallow");
   static_assert(LDS <= SMALL_LDS_BUDGET, "LDS budget");
   static_assert((D - 3) * (NCB + ACH + (TG ? 2 : 1)) < 64, "vmcnt range");
+  // 32x32 scales: wave 0 loads the whole round's scale record with one direct
+  // load; SCL = scale loads per round of the other waves
+  static constexpr bool ROUND_SC = !TG;
+  static constexpr int SCL = ROUND_SC ? 0 : (TG ? 2 : 1);
 };
 
 template <int MT, int NCB, bool TG>
@@ -1214,9 +1218,13 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
     a_live += 4 * (w + 8 * ch) < M ? 1 : 0;
   }
   const int nrb = (int)((M + 31) >> 5);
-  const int sbj = lane - 2 < NCB - 1 ? (lane - 2 > 0 ? lane - 2 : 0) : NCB - 1;
-  const float* const sc_src =
-      lane < 2 ? sa + (int64_t)(lane < nrb ? lane : nrb - 1) * KB : sbt + (int64_t)(cb0 + sbj) * KB;
+  // round record (wave 0), as in gemm_smallm_nt_kernel: lane l < 16 = sa of
+  // row-block min(l >> 3, nrb-1) at K-block 8r + (l & 7); lane 16 + q*NCB + c =
+  // sbt of column block cb0 + c at K-block 8r + q; K-blocks clamped to the last
+  const int rs_l = lane < 16 ? lane : (lane - 16 < 8 * NCB ? lane - 16 : 8 * NCB - 1);
+  const int rs_q = lane < 16 ? (rs_l & 7) : rs_l / NCB;
+  const float* const rs_src = lane < 16 ? sa + (int64_t)((lane >> 3) < nrb ? (lane >> 3) : nrb - 1) * KB
+                                        : sbt + (int64_t)(cb0 + rs_l % NCB) * KB;
   const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
   const float* const tg_sb_src = sbt + (int64_t)(cb0 + (lane < NCB ? lane : NCB - 1)) * KB;
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -1240,7 +1248,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
       dma4(tg_sa_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
       dma4(tg_sb_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC + 256);
     } else {
-      dma4(sc_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
+      if (w == 0) {
+        int kr = r * SWAVES + rs_q;
+        kr = kr < KB ? kr : KB - 1;
+        dma4(rs_src + kr, sl + Cfg::SC_OFF);
+      }
     }
   };
 
@@ -1300,7 +1312,9 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
           const int e = G + STHREADS * j;
           const float p = *reinterpret_cast<const float*>(pb + (q * T + (e >> 8)) * 1024 + (e & 255) * 4);
           const int own_cb = e_col[j] >> 5;
-          const float sc = (TG ? scr[e_row[j]] : scr[e_row[j] >> 5]) * scr[(TG ? 64 : 2) + own_cb];
+          const float* rec = reinterpret_cast<const float*>(sl + Cfg::SC_OFF);  // wave 0's round record
+          const float sc = TG ? scr[e_row[j]] * scr[64 + own_cb]
+                              : rec[8 * (e_row[j] >> 5) + q] * rec[16 + q * NCB + own_cb];
           acc[j] = __builtin_fmaf(p, sc, acc[j]);
         }
       }
@@ -1314,10 +1328,16 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
   }
   for (int r = 0; r < rounds; ++r) {
     // this wave's round-r loads have landed: NCB + a_live + scale loads per round, D - 3 rounds may be pending
-    constexpr int LB = (D - 3) * (NCB + (TG ? 2 : 1));
+    constexpr int LB = (D - 3) * (NCB + Cfg::SCL);
+    constexpr int LB0 = Cfg::ROUND_SC ? D - 3 : 0;  // wave 0's round records (wave 0 always loads A)
     if (a_live == 0) wait_vmcnt<LB>();
-    else if (a_live == 1) wait_vmcnt<LB + (D - 3)>();
-    else wait_vmcnt<LB + 2 * (D - 3)>();
+    else if (a_live == 1) {
+      if (w == 0) wait_vmcnt<LB + LB0 + (D - 3)>();
+      else wait_vmcnt<LB + (D - 3)>();
+    } else {
+      if (w == 0) wait_vmcnt<LB + LB0 + 2 * (D - 3)>();
+      else wait_vmcnt<LB + 2 * (D - 3)>();
+    }
     lds_barrier();   // round r visible; round r-1's partials visible; round r-2's slot free
     issue(r + D - 2);
     // Promotion of round r-1 first: its partial and scale reads then precede
