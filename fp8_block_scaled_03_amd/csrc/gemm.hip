@@ -1173,8 +1173,13 @@ struct SmallMNtSplitCfg {
   static_assert((D - 3) * (NCB + ACH + (TG ? 2 : 1)) < 64, "vmcnt range");
   // 32x32 scales: wave 0 loads the whole round's scale record with one direct
   // load; SCL = scale loads per round of the other waves
-  static constexpr bool ROUND_SC = !TG;
-  static constexpr int SCL = ROUND_SC ? 0 : (TG ? 2 : 1);
+  // token-group scales (at most 16 rows here): waves 0 and 1 load sa of rows
+  // 0-7 and 8-15 for the round's eight K-blocks, wave 2 the sb entries, one
+  // direct load each; RSW = waves that load a round record
+  static constexpr bool ROUND_SC = true;
+  static constexpr int SCL = 0;
+  static constexpr int RSW = TG ? 3 : 1;
+  static_assert(!TG || MT == 1, "token-group round records hold 16 rows");
 };
 
 template <int MT, int NCB, bool TG>
@@ -1225,8 +1230,15 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
   const int rs_q = lane < 16 ? (rs_l & 7) : rs_l / NCB;
   const float* const rs_src = lane < 16 ? sa + (int64_t)((lane >> 3) < nrb ? (lane >> 3) : nrb - 1) * KB
                                         : sbt + (int64_t)(cb0 + rs_l % NCB) * KB;
-  const float* const tg_sa_src = sa + (int64_t)(lane < M ? lane : M - 1) * KB;
-  const float* const tg_sb_src = sbt + (int64_t)(cb0 + (lane < NCB ? lane : NCB - 1)) * KB;
+  // token-group round records: wave w < 2, lane l = sa of row 8w + (l >> 3)
+  // (clamped to M-1) at K-block 8r + (l & 7); wave 2, lane l = sbt of column
+  // block cb0 + c at K-block 8r + q for l = q * NCB + c (lanes past 8 * NCB
+  // repeat the last entry); both step 1 per K-block
+  const int tg_l = lane < 8 * NCB ? lane : 8 * NCB - 1;
+  const int tg_q = w < 2 ? (lane & 7) : tg_l / NCB;
+  const int tg_row = 8 * w + (lane >> 3);
+  const float* const tg_rs_src = w < 2 ? sa + (int64_t)(tg_row < M ? tg_row : M - 1) * KB
+                                       : sbt + (int64_t)(cb0 + tg_l % NCB) * KB;
   typedef __attribute__((address_space(3))) unsigned char lds_u8;
   const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
 
@@ -1245,8 +1257,11 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
     int kc = r * SWAVES + w;
     kc = kc < KB ? kc : KB - 1;
     if constexpr (TG) {
-      dma4(tg_sa_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC);
-      dma4(tg_sb_src + kc, sl + Cfg::SC_OFF + w * Cfg::REC + 256);
+      if (w < 3) {
+        int kr = r * SWAVES + tg_q;
+        kr = kr < KB ? kr : KB - 1;
+        dma4(tg_rs_src + kr, sl + Cfg::SC_OFF + w * Cfg::REC);
+      }
     } else {
       if (w == 0) {
         int kr = r * SWAVES + rs_q;
@@ -1306,14 +1321,16 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
 #pragma unroll
     for (int q = 0; q < SWAVES; ++q) {
       if (q < nkb) {
-        const float* scr = reinterpret_cast<const float*>(sl + Cfg::SC_OFF + q * Cfg::REC);
 #pragma unroll
         for (int j = 0; j < EPL; ++j) {
           const int e = G + STHREADS * j;
           const float p = *reinterpret_cast<const float*>(pb + (q * T + (e >> 8)) * 1024 + (e & 255) * 4);
           const int own_cb = e_col[j] >> 5;
-          const float* rec = reinterpret_cast<const float*>(sl + Cfg::SC_OFF);  // wave 0's round record
-          const float sc = TG ? scr[e_row[j]] * scr[64 + own_cb]
+          // round records: 32x32 scales in wave 0's; token groups: sa of row r
+          // in wave (r >> 3)'s at lane (r & 7) * 8 + q, sb in wave 2's
+          const float* rec = reinterpret_cast<const float*>(sl + Cfg::SC_OFF);
+          const float sc = TG ? rec[(e_row[j] >> 3) * (Cfg::REC / 4) + (e_row[j] & 7) * 8 + q] *
+                                    rec[2 * (Cfg::REC / 4) + q * NCB + own_cb]
                               : rec[8 * (e_row[j] >> 5) + q] * rec[16 + q * NCB + own_cb];
           acc[j] = __builtin_fmaf(p, sc, acc[j]);
         }
@@ -1329,13 +1346,17 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
   for (int r = 0; r < rounds; ++r) {
     // this wave's round-r loads have landed: NCB + a_live + scale loads per round, D - 3 rounds may be pending
     constexpr int LB = (D - 3) * (NCB + Cfg::SCL);
-    constexpr int LB0 = Cfg::ROUND_SC ? D - 3 : 0;  // wave 0's round records (wave 0 always loads A)
-    if (a_live == 0) wait_vmcnt<LB>();
-    else if (a_live == 1) {
-      if (w == 0) wait_vmcnt<LB + LB0 + (D - 3)>();
+    // round records: waves below RSW load one per round
+    constexpr int LB0 = D - 3;
+    const bool rs = w < Cfg::RSW;
+    if (a_live == 0) {
+      if (rs) wait_vmcnt<LB + LB0>();
+      else wait_vmcnt<LB>();
+    } else if (a_live == 1) {
+      if (rs) wait_vmcnt<LB + LB0 + (D - 3)>();
       else wait_vmcnt<LB + (D - 3)>();
     } else {
-      if (w == 0) wait_vmcnt<LB + LB0 + 2 * (D - 3)>();
+      if (rs) wait_vmcnt<LB + LB0 + 2 * (D - 3)>();
       else wait_vmcnt<LB + 2 * (D - 3)>();
     }
     lds_barrier();   // round r visible; round r-1's partials visible; round r-2's slot free
