@@ -100,8 +100,9 @@ def test_gemm_nt_empty_k():
         assert c.shape == (m, 64) and np.all(c == 0)
 
 
-def test_grouped_nt_matches_oracle_and_kn_path():
-    G, K, N = 5, 128, 96
+@pytest.mark.parametrize("K", [128, 96, 32])   # even, odd and single K-block counts
+def test_grouped_nt_matches_oracle_and_kn_path(K):
+    G, N = 5, 96
     rows = np.array([64, 0, 288, 32, 96])
     off = W.offsets_from_rows(rows)
     M = int(off[-1])
@@ -110,7 +111,7 @@ def test_grouped_nt_matches_oracle_and_kn_path():
     sb = np.stack([_quantized(71 + i, K, N, std=0.02)[1] for i in range(G)])
     qbt = np.ascontiguousarray(qb.transpose(0, 2, 1))
     sbt = np.ascontiguousarray(sb.transpose(0, 2, 1))
-    say("grouped_nt small")
+    say(f"grouped_nt small K={K}")
     c = gpu_grouped_nt(qa, sa, qbt, sbt, off)
     ref, absref = oracle.grouped_gemm_ref_nt(qa, sa, qbt, sbt, off)
     _assert_tol(c, ref, absref, "grouped nt")
