@@ -178,3 +178,49 @@ def test_gemm_e8m0_small_m_wide_weight():
     for m in (3, 16, 40):
         part = gpu_gemm_e8m0(qa[:m], ea[:-(-m // 32)], qbt, ebt)
         assert np.array_equal(part, full[:m]), m
+
+
+def test_gemm_e8m0_decode_and_prefill_full_size_sampled():
+    """Decode K = 8192 (M = 64 and its prefixes, N = 8192 and 28672) and a
+    prefill slab (M = K = 8192, N = 10240), both operands quantized on the GPU:
+    prefixes bitwise equal to the full rows, sampled 32x32 output blocks
+    within the bound against the oracle, which quantizes the slabs itself."""
+    for N in (8192, 28672):
+        wl = W.decode(64, N)
+        a_bits = wl.a_bits()
+        bt_bits = np.ascontiguousarray(wl.b_bits().T)
+        say(f"decode e8m0 N={N}")
+        qa, ea = fp8bs.quantize_e8m0(bf16_dev(a_bits))
+        qbt, ebt = fp8bs.quantize_e8m0(bf16_dev(bt_bits))
+        c = fp8bs.gemm_e8m0_nt(qa, ea, qbt, ebt)
+        torch.cuda.synchronize()
+        for m in (1, 8, 32):
+            cm = fp8bs.gemm_e8m0_nt(qa[:m].contiguous(), ea[:1].contiguous(), qbt, ebt)
+            torch.cuda.synchronize()
+            assert torch.equal(cm.view(torch.int16), c[:m].view(torch.int16)), f"N={N} M={m}"
+        qa_o, ea_o = oracle.quantize_blocks_e8m0(a_bits)
+        for cb in (0, N // 32 - 1, 77):
+            cols = slice(cb * 32, cb * 32 + 32)
+            qbt_o, ebt_o = oracle.quantize_blocks_e8m0(bt_bits[cols])
+            ref, absref = oracle.gemm_ref_e8m0_nt(qa_o, ea_o, qbt_o, ebt_o)
+            ok = e8m0_ok(bits_np(c[:, cols].contiguous()), ref, absref)
+            assert ok.all(), f"decode e8m0 N={N} block {cb}"
+        del qa, ea, qbt, ebt, c
+        torch.cuda.empty_cache()
+    wl = W.prefill(10240)
+    a_bits = wl.a_bits()
+    bt_bits = np.ascontiguousarray(wl.b_bits().T)
+    say("prefill e8m0 N=10240")
+    qa, ea = fp8bs.quantize_e8m0(bf16_dev(a_bits))
+    qbt, ebt = fp8bs.quantize_e8m0(bf16_dev(bt_bits))
+    c = fp8bs.gemm_e8m0_nt(qa, ea, qbt, ebt)
+    torch.cuda.synchronize()
+    for rb in (0, 255, 101):
+        rows = slice(rb * 32, rb * 32 + 32)
+        qa_o, ea_o = oracle.quantize_blocks_e8m0(a_bits[rows])
+        for cb in (0, 319, 150):
+            cols = slice(cb * 32, cb * 32 + 32)
+            qbt_o, ebt_o = oracle.quantize_blocks_e8m0(bt_bits[cols])
+            ref, absref = oracle.gemm_ref_e8m0_nt(qa_o, ea_o, qbt_o, ebt_o)
+            ok = e8m0_ok(bits_np(c[rows, cols].contiguous()), ref, absref)
+            assert ok.all(), f"prefill e8m0 block ({rb},{cb})"
