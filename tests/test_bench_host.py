@@ -20,3 +20,26 @@ def test_current_sclk_deep_sleep_level():
 def test_current_sclk_no_marked_level():
     assert bench.current_sclk_mhz("0: 500Mhz\n1: 2400Mhz\n") is None
     assert bench.current_sclk_mhz("") is None
+
+
+def test_committed_counter_summaries_match_current_sources():
+    """Every HBM-traffic and SQ-counter summary under profiles/ records the hash
+    of the kernel sources it was measured on; a kernel edit must come with
+    fresh counters (the bench reads the tile kernel's traffic only when its
+    hash matches, the other summaries are cited as they stand)."""
+    import glob
+    import os
+    from fp8_block_scaled_03_amd import profiling
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = sorted(glob.glob(os.path.join(root, "profiles", "traffic_*.txt")) +
+                   glob.glob(os.path.join(root, "profiles", "counters_*.txt")))
+    assert files
+    for path in files:
+        fields = {}
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        sources = fields.get("sources", " ".join(profiling.GEMM_SOURCES)).split()
+        assert fields.get("source_sha") == profiling.source_sha(sources), os.path.basename(path)
