@@ -6,10 +6,19 @@ block-scaled GEMM to bf16 C, on the square 4096 x 4096 x 4096 workload (inputs
 N(0,1), seeded, already resident in HBM).  `value` is 2*M*N*K per step over the
 measured step time (TFLOP/s of the whole path).
 
-Also measured (same run, reported under "detail"):
-  * the GEMM kernel alone, per launch with HIP events on the launch stream, with
-    the caches flushed before each launch (a 1 GiB read), and its roofline
-    against MI355X's dense FP8 MFMA peak;
+"roofline" is the GEMM kernel of the timed steps: HIP events on the launch
+stream around the GEMM launch of every timed step, their mean against
+MI355X's dense FP8 MFMA peak.  `--roofline-only` runs just the warm-up and the
+timed steps, so that a rocprofv3 kernel trace of it averages exactly those
+launches.
+
+Also measured (same run, reported under "detail"; median and min per entry):
+  * the GEMM kernel alone, per launch with the caches flushed before each
+    launch (a 1 GiB read), and the streaming-read rate of that flush read,
+    which the decode rows are also reported against;
+  * the square 256^3 workload in microseconds (GEMM alone and the whole step);
+  * the prefill GEMM, M = K = 8192, N in {10240, 8192, 28672}, and the grouped
+    GEMM (G = 16, K = 7168, N = 4096, 8192 rows);
   * the small-M (decode) GEMM at K=8192, M in {1, 8, 32, 64}, N in
     {8192, 28672}: algorithmic HBM bytes per launch over the kernel time;
   * the quantizer alone (HBM bytes per launch over its time);
@@ -22,7 +31,8 @@ Also measured (same run, reported under "detail"):
   * the CPU oracle on a bounded sample of the same workload ("cpu_baseline").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
-       python bench.py --profile-kernels   (a short run for rocprofv3 passes)
+       python bench.py --roofline-only      (the timed steps only, for the kernel trace)
+       python bench.py --profile-kernels    (a short run for rocprofv3 counter passes)
 """
 
 from __future__ import annotations
@@ -61,6 +71,9 @@ def parse():
                         "would dominate the kernel statistics)")
     p.add_argument("--profile-kernels", action="store_true",
                    help="run each kernel a few times without timing (for rocprofv3 counter passes)")
+    p.add_argument("--roofline-only", action="store_true",
+                   help="only the warm-up and timed steps and the JSON line (for the rocprofv3 kernel-trace "
+                        "summary of the roofline kernel: every GEMM launch of the run is then a step launch)")
     return p.parse_args()
 
 
@@ -223,22 +236,32 @@ def main():
         print(json.dumps({"profile_kernels": "done", "copy_bytes": 256 << 20}))
         return
 
+    # The GEMM launch of every timed step is bracketed by HIP events on the
+    # launch stream; the roofline figure is their mean.  (Recording an event
+    # costs the GPU nothing measurable; the step time is the wall clock.)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def timed_step(i):
+        fp8bs.quantize(a, qa, sa)
+        fp8bs.quantize(b, qb, sb)
+        ev[i][0].record(stream)
+        fp8bs.gemm(qa, sa, qb, sb, out=c)
+        ev[i][1].record(stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        timed_step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
+    step_gemm_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    g_avg = sum(step_gemm_ms) / len(step_gemm_ms)
 
-    reps = 10 if args.quick else args.reps
-    for _ in range(5):
-        gemm_only()
-    g_med, g_min, g_avg = time_launch(gemm_only, reps)
-    q_med, q_min, q_avg = time_launch(lambda: fp8bs.quantize(a, qa, sa), reps)
     gemm_flops = 2.0 * M * N * K
     # algorithmic bytes of one GEMM launch: A + B (E4M3) + both scale grids + C (bf16)
     gemm_bytes = M * K + K * N + 4 * (M // 32) * (K // 32) + 4 * (K // 32) * (N // 32) + 2 * M * N
@@ -256,16 +279,80 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": "gemm_tile_kernel", "per_launch_flops": gemm_flops, "per_launch_alg_bytes": gemm_bytes,
-                "avg_ms": round(g_avg, 5)}
+                "avg_ms": round(g_avg, 5), "launches": len(step_gemm_ms),
+                "timing": "HIP events around the GEMM launch of every timed step, on its stream"}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (exact bf16 MFMA products, fp32 accumulation)",
+        "data": "synthetic",
+        "config": {"workload": "square-4096: quantize A, B (bf16 -> E4M3, 32x32 scales) + block-scaled GEMM",
+                   "M": M, "N": N, "K": K, "block": 32, "seed": wl.seed},
+        "roofline": roofline,
+    }
+    if args.roofline_only:
+        print(json.dumps(out), flush=True)
+        return
+
+    reps = 10 if args.quick else args.reps
+
+    def ms_entry(med, mn):
+        return {"median": round(med, 5), "min": round(mn, 5)}
+
+    # streaming-read ceiling of this GPU in this run: the cache flush itself
+    # (a read of 1 GiB)
+    flush()
+    fl_med, fl_min, _ = time_launch(flush, 10, do_flush=False)
+    stream_gbs = flush_buf.numel() * 4 / (fl_med * 1e-3) / 1e9
+
+    for _ in range(5):
+        gemm_only()
+    g_med, g_min, g_favg = time_launch(gemm_only, reps)
+    q_med, q_min, q_avg = time_launch(lambda: fp8bs.quantize(a, qa, sa), reps)
 
     detail = {
         "sclk_mhz_during_gemm": None if args.no_sclk else sample_sclk(gemm_only, torch),
-        "gemm_kernel_ms": {"median": round(g_med, 5), "min": round(g_min, 5), "mean": round(g_avg, 5)},
-        "gemm_kernel_tflops_median": round(gemm_flops / (g_med * 1e-3) / 1e12, 1),
+        "gemm_in_step_ms": {"median": round(step_gemm_ms[len(step_gemm_ms) // 2], 5),
+                            "min": round(step_gemm_ms[0], 5), "mean": round(g_avg, 5)},
+        "gemm_flushed_ms": {"median": round(g_med, 5), "min": round(g_min, 5), "mean": round(g_favg, 5)},
+        "gemm_flushed_tflops_median": round(gemm_flops / (g_med * 1e-3) / 1e12, 1),
         "gemm_frac_of_bf16_mfma_peak": round(achieved / BF16_DENSE_PEAK_TFLOPS, 4),
-        "quantize_4096x4096_ms_median": round(q_med, 5),
+        "quantize_4096x4096_ms": ms_entry(q_med, q_min),
         "quantize_4096x4096_gbs": round(3.0 * M * K / (q_med * 1e-3) / 1e9, 1),
+        "stream_read_ceiling": {"gbs": round(stream_gbs, 1), "frac_hbm_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
+                                "what": "the 1 GiB cache-flush read (a max reduction), median of 10"},
     }
+
+    # square 256^3 (quantize both operands + GEMM, and the GEMM alone): a
+    # launch-latency-bound size, reported in microseconds
+    s_wl = W.square_256()
+    s_a, s_b = to_dev_bf16(s_wl.a_bits()), to_dev_bf16(s_wl.b_bits())
+    s_qa, s_sa = fp8bs.quantize(s_a)
+    s_qb, s_sb = fp8bs.quantize(s_b)
+    s_c = torch.empty((256, 256), dtype=torch.bfloat16, device=dev)
+    s_gemm = lambda: fp8bs.gemm(s_qa, s_sa, s_qb, s_sb, out=s_c)
+    s_step = lambda: (fp8bs.quantize(s_a, s_qa, s_sa), fp8bs.quantize(s_b, s_qb, s_sb), s_gemm())
+    for _ in range(5):
+        s_step()
+    sg_med, sg_min, _ = time_launch(s_gemm, reps)
+    ss_med, ss_min, _ = time_launch(s_step, reps)
+    detail["square_256"] = {"gemm_us": {"median": round(sg_med * 1e3, 2), "min": round(sg_min * 1e3, 2)},
+                            "step_us": {"median": round(ss_med * 1e3, 2), "min": round(ss_min * 1e3, 2)}}
+    del s_a, s_b, s_qa, s_sa, s_qb, s_sb, s_c
+
+    def decode_entry(m, n_dec, k, nbytes, d_med, d_min):
+        gbs = nbytes / (d_med * 1e-3) / 1e9
+        return {"M": m, "N": n_dec, "K": k, "median_us": round(d_med * 1e3, 2), "min_us": round(d_min * 1e3, 2),
+                "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "frac_stream_read": round(gbs / stream_gbs, 4)}
 
     if not args.quick:
         def decode_sweep(k_major, token_groups):
@@ -289,9 +376,7 @@ def main():
                         fn()
                     d_med, d_min, d_avg = time_launch(fn, reps)
                     nbytes = m * dwl.K + dwl.K * n_dec + 4 * sa_rows * KB + 4 * KB * (n_dec // 32) + 2 * m * n_dec
-                    rows_out.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
-                                     "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
-                                     "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                    rows_out.append(decode_entry(m, n_dec, dwl.K, nbytes, d_med, d_min))
                 del q64, s64, dqw, dsw
             return rows_out
 
@@ -303,15 +388,15 @@ def main():
         # per-token-group activation scales (1 x 32): quantizer, square GEMM, decode
         sa_tg = torch.empty((M, K // 32), dtype=torch.float32, device=dev)
         fp8bs.quantize_tg(a, qa, sa_tg)
-        tq_med, _, _ = time_launch(lambda: fp8bs.quantize_tg(a, qa, sa_tg), reps)
+        tq_med, tq_min, _ = time_launch(lambda: fp8bs.quantize_tg(a, qa, sa_tg), reps)
         tg_fn = lambda: fp8bs.gemm_tg(qa, sa_tg, qb, sb, out=c)
         for _ in range(3):
             tg_fn()
-        tg_med, _, tg_avg = time_launch(tg_fn, reps)
+        tg_med, tg_min, tg_avg = time_launch(tg_fn, reps)
         detail["token_groups"] = {
-            "quantize_tg_4096x4096_ms_median": round(tq_med, 5),
+            "quantize_tg_4096x4096_ms": ms_entry(tq_med, tq_min),
             "quantize_tg_4096x4096_gbs": round((2 * M * K + M * K + 4 * M * (K // 32)) / (tq_med * 1e-3) / 1e9, 1),
-            "gemm_tg_4096_ms_median": round(tg_med, 5),
+            "gemm_tg_4096_ms": ms_entry(tg_med, tg_min),
             "gemm_tg_4096_tflops_median": round(gemm_flops / (tg_med * 1e-3) / 1e12, 1),
             "decode_k_major_weight": decode_sweep(True, True),
             "decode": decode_sweep(False, True),
@@ -331,25 +416,31 @@ def main():
                                                             scales=ns[:m]))
                 for _ in range(3):
                     fn()
-                n_med, _, _ = time_launch(fn, reps)
+                n_med, n_min, _ = time_launch(fn, reps)
                 nbytes = m * (7 * nwl.d + 4 * (nwl.d // 32)) + 2 * nwl.d
                 norm.append({"rows": m, "d": nwl.d, "median_us": round(n_med * 1e3, 2),
+                             "min_us": round(n_min * 1e3, 2),
                              "gbs": round(nbytes / (n_med * 1e-3) / 1e9, 1),
                              "frac_hbm_peak": round(nbytes / (n_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
             del nx, nr, ng, nq, ns
         detail["rmsnorm_residual_quantize_tg"] = norm
 
-        # prefill M = K = 8192, N = 28672 and the grouped workload (GEMM only)
-        pwl = W.prefill(28672)
-        pqa, psa = fp8bs.quantize(to_dev_bf16(pwl.a_bits()))
-        pqb, psb = fp8bs.quantize(to_dev_bf16(pwl.b_bits()))
-        pc = torch.empty((pwl.M, pwl.N), dtype=torch.bfloat16, device=dev)
-        pfn = lambda: fp8bs.gemm(pqa, psa, pqb, psb, out=pc)
-        pfn()
-        p_med, _, _ = time_launch(pfn, 10)
-        detail["prefill_M8192_K8192_N28672"] = {"median_ms": round(p_med, 4),
-                                                "tflops": round(pwl.flops() / (p_med * 1e-3) / 1e12, 1)}
-        del pqa, psa, pqb, psb, pc
+        # prefill M = K = 8192, N in {10240, 8192, 28672}, and the grouped
+        # workload (GEMM only)
+        pqa, psa = fp8bs.quantize(to_dev_bf16(W.prefill(8192).a_bits()))
+        prefill = []
+        for n_pre in (10240, 8192, 28672):
+            pwl = W.prefill(n_pre)
+            pqb, psb = fp8bs.quantize(to_dev_bf16(pwl.b_bits()))
+            pc = torch.empty((pwl.M, pwl.N), dtype=torch.bfloat16, device=dev)
+            pfn = lambda: fp8bs.gemm(pqa, psa, pqb, psb, out=pc)
+            pfn()
+            p_med, p_min, _ = time_launch(pfn, 20)
+            prefill.append({"M": pwl.M, "N": n_pre, "K": pwl.K, "median_ms": round(p_med, 4),
+                            "min_ms": round(p_min, 4), "tflops": round(pwl.flops() / (p_med * 1e-3) / 1e12, 1)})
+            del pqb, psb, pc
+        detail["prefill_K8192_M8192"] = prefill
+        del pqa, psa
         gwl = W.grouped()
         off = gwl.offsets()
         gqa, gsa = fp8bs.quantize(to_dev_bf16(gwl.a_bits()))
@@ -360,9 +451,9 @@ def main():
         gc = torch.empty((gwl.M, gwl.N), dtype=torch.bfloat16, device=dev)
         gfn = lambda: fp8bs.grouped_gemm(gqa, gsa, gqb, gsb, goff, out=gc)
         gfn()
-        g_med2, _, _ = time_launch(gfn, 10)
+        g_med2, g_min2, _ = time_launch(gfn, 20)
         live = int(np.count_nonzero(np.diff(off)))
-        detail["grouped_G16_M8192_K7168_N4096"] = {"median_ms": round(g_med2, 4),
+        detail["grouped_G16_M8192_K7168_N4096"] = {"median_ms": round(g_med2, 4), "min_ms": round(g_min2, 4),
                                                    "tflops": round(gwl.flops() / (g_med2 * 1e-3) / 1e12, 1),
                                                    "live_groups": live}
         del gqa, gsa, gqb2, gsb2, gc
@@ -374,14 +465,14 @@ def main():
         eqa, eea = fp8bs.quantize_e8m0(a)
         eqb, eeb = fp8bs.quantize_e8m0(to_dev_bf16(bt_sq))
         del bt_sq
-        eq_med, _, _ = time_launch(lambda: fp8bs.quantize_e8m0(a, eqa, eea), reps)
-        e8["quantize_e8m0_4096x4096_ms_median"] = round(eq_med, 5)
+        eq_med, eq_min, _ = time_launch(lambda: fp8bs.quantize_e8m0(a, eqa, eea), reps)
+        e8["quantize_e8m0_4096x4096_ms"] = ms_entry(eq_med, eq_min)
         e8["quantize_e8m0_4096x4096_gbs"] = round((3 * M * K + (M // 32) * (K // 32)) / (eq_med * 1e-3) / 1e9, 1)
         efn = lambda: fp8bs.gemm_e8m0_nt(eqa, eea, eqb, eeb, out=c)
         for _ in range(3):
             efn()
-        e_med, _, _ = time_launch(efn, reps)
-        e8["gemm_e8m0_4096_ms_median"] = round(e_med, 5)
+        e_med, e_min, _ = time_launch(efn, reps)
+        e8["gemm_e8m0_4096_ms"] = ms_entry(e_med, e_min)
         e8["gemm_e8m0_4096_tflops_median"] = round(gemm_flops / (e_med * 1e-3) / 1e12, 1)
         del eqa, eea, eqb, eeb
         pwl = W.prefill(28672)
@@ -390,8 +481,8 @@ def main():
         pc = torch.empty((pwl.M, pwl.N), dtype=torch.bfloat16, device=dev)
         pfn = lambda: fp8bs.gemm_e8m0_nt(pqa, pea, pqb, peb, out=pc)
         pfn()
-        pe_med, _, _ = time_launch(pfn, 10)
-        e8["prefill_M8192_K8192_N28672"] = {"median_ms": round(pe_med, 4),
+        pe_med, pe_min, _ = time_launch(pfn, 20)
+        e8["prefill_M8192_K8192_N28672"] = {"median_ms": round(pe_med, 4), "min_ms": round(pe_min, 4),
                                             "tflops": round(pwl.flops() / (pe_med * 1e-3) / 1e12, 1)}
         del pqa, pea, pqb, peb, pc
         e8_dec = []
@@ -407,11 +498,9 @@ def main():
                 fn = (lambda dqa=dqa, dea=dea, dc=dc: fp8bs.gemm_e8m0_nt(dqa, dea, dqw, dew, out=dc))
                 for _ in range(3):
                     fn()
-                d_med, _, _ = time_launch(fn, reps)
+                d_med, d_min, _ = time_launch(fn, reps)
                 nbytes = m * dwl.K + dwl.K * n_dec + ea_rows * KB + KB * (n_dec // 32) + 2 * m * n_dec
-                e8_dec.append({"M": m, "N": n_dec, "K": dwl.K, "median_us": round(d_med * 1e3, 2),
-                               "gbs": round(nbytes / (d_med * 1e-3) / 1e9, 1),
-                               "frac_hbm_peak": round(nbytes / (d_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+                e8_dec.append(decode_entry(m, n_dec, dwl.K, nbytes, d_med, d_min))
             del q64, e64, dqw, dew
         e8["decode_k_major_weight"] = e8_dec
         detail["e8m0"] = e8
@@ -427,10 +516,10 @@ def main():
         lfn = lambda: fp8bs.gemm_nt(lqa, lsa, lqw, lsw, out=lc)
         for _ in range(3):
             lfn()
-        l_med, _, _ = time_launch(lfn, reps)
+        l_med, l_min, _ = time_launch(lfn, reps)
         lbytes = 8 * lwl.K + lwl.K * 28672 + 4 * (lwl.K // 32) + 4 * (lwl.K // 32) * (28672 // 32) + 2 * 8 * 28672
         detail["decode_k_major_weight_allocated_late"] = {
-            "M": 8, "N": 28672, "K": lwl.K, "median_us": round(l_med * 1e3, 2),
+            "M": 8, "N": 28672, "K": lwl.K, "median_us": round(l_med * 1e3, 2), "min_us": round(l_min * 1e3, 2),
             "gbs": round(lbytes / (l_med * 1e-3) / 1e9, 1)}
         del lq64, ls64, lqw, lsw, lqa, lsa, lc
 
@@ -438,25 +527,8 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(wl)
 
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "e4m3 (exact bf16 MFMA products, fp32 accumulation)",
-        "data": "synthetic",
-        "config": {"workload": "square-4096: quantize A, B (bf16 -> E4M3, 32x32 scales) + block-scaled GEMM",
-                   "M": M, "N": N, "K": K, "block": 32, "seed": wl.seed},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "detail": detail,
-    }
+    out["cpu_baseline"] = cpu
+    out["detail"] = detail
     print(json.dumps(out), flush=True)
 
 
@@ -528,9 +600,12 @@ def cpu_baseline(wl):
     qb, sb = oracle.quantize_blocks(b_bits)
     oracle.gemm_ref(qa, sa, qb, sb)
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')}, {i.get('num_threads')} threads)"
+            for i in info if i.get("user_api") == "blas"]
     return {"value": round(2.0 * rows * wl.N * wl.K / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
+            "kind": "oracle", "seconds": round(dt, 2), "blas": "; ".join(blas) or None,
             "sample": f"square-4096 step restricted to A rows 0..{rows - 1}: oracle quantize (A rows, all of B) "
                       f"+ fp64 reference GEMM {rows}x{wl.N}x{wl.K}",
             "host_cpus": len(os.sched_getaffinity(0))}

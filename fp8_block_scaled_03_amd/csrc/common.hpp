@@ -11,7 +11,7 @@
 //     K-blocks in ascending order into one fp32 accumulator
 //     (DeepGEMM write-up on hncyxsy.com, sections 2.2-2.3: the block scales
 //     enter during accumulation, not in a separate pass over C);
-//   * C = bf16(acc), round to nearest even, once.
+//   * C = bf16(acc), round to nearest even, once; an exact zero is stored as +0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,6 +73,13 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+
+// A GEMM output element: bf16(acc) with an exact zero stored as +0.  acc + 0
+// turns -0 into +0 and leaves every other value unchanged, so the sign of a
+// zero result never depends on which kernel formed it (a kernel that promotes
+// an extra zero-scale K-block and one that does not may otherwise differ in
+// the sign of an exact zero).
+__device__ __forceinline__ uint32_t bf16_out(float acc) { return bf16_rne(acc + 0.0f); }
 
 // ---- E4M3 quantizer steps shared by every kernel that writes codes --------------------
 // Groups with amax at or above this value take the reciprocal path below.

@@ -413,9 +413,10 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // would give the loop's back edge two different orders of loads in flight,
   // and the compiler would then wait for all of them before staging.  An odd
   // last K-block is paired with an empty one (kb = KB) whose scale products
-  // are zero: fma(P, 0, acc) returns acc bit for bit, since P is finite (a
-  // partial of finite codes) and acc is never -0 (it starts at +0, and an
-  // exact cancellation rounds to +0).
+  // are zero: fma(P, 0, acc) returns acc for every nonzero acc, since P is
+  // finite (a partial of finite codes).  A zero acc may change sign there;
+  // the epilogue stores every exact zero as +0 (bf16_out), so the stored bits
+  // equal those of a kernel that stops at the last K-block.
   if (p.row0 + wm * 64 < p.row_end) {
     for (int kb = 0; kb < KB; kb += 2) {
       iteration(kb, ra, rb, std::true_type{});
@@ -442,15 +443,15 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
           // lane holds row ii*16 + (lane&15), columns j*16 + 4*(lane>>4) + 0..3
           const int lr = ii * 16 + (lane & 15);
           const int lc = j * 16 + 4 * (lane >> 4);
-          const uint32_t lo = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-          const uint32_t hi = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          const uint32_t lo = bf16_out(acc[i][j][0]) | (bf16_out(acc[i][j][1]) << 16);
+          const uint32_t hi = bf16_out(acc[i][j][2]) | (bf16_out(acc[i][j][3]) << 16);
           *reinterpret_cast<uint2*>(ep + lr * 256 + lc * 2) = make_uint2(lo, hi);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int lr = ii * 16 + 4 * (lane >> 4) + r;
             const int lc = j * 16 + (lane & 15);
-            *reinterpret_cast<uint16_t*>(ep + lr * 256 + lc * 2) = (uint16_t)bf16_rne(acc[i][j][r]);
+            *reinterpret_cast<uint16_t*>(ep + lr * 256 + lc * 2) = (uint16_t)bf16_out(acc[i][j][r]);
           }
         }
       }
@@ -840,8 +841,8 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
         const int64_t row = i * 16 + (lane & 15);
         const int64_t col4 = n0 + cs * 16 + 4 * (lane >> 4);
         if (row < M) {
-          const uint32_t lo = bf16_rne(acc[t][0]) | (bf16_rne(acc[t][1]) << 16);
-          const uint32_t hi = bf16_rne(acc[t][2]) | (bf16_rne(acc[t][3]) << 16);
+          const uint32_t lo = bf16_out(acc[t][0]) | (bf16_out(acc[t][1]) << 16);
+          const uint32_t hi = bf16_out(acc[t][2]) | (bf16_out(acc[t][3]) << 16);
           *reinterpret_cast<uint2*>(c + row * N + col4) = make_uint2(lo, hi);
         }
       } else {
@@ -849,7 +850,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
-          if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+          if (row < M) c[row * N + col] = (uint16_t)bf16_out(acc[t][rr]);
         }
       }
     }
@@ -1122,8 +1123,8 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
         const int64_t row = i * 16 + (lane & 15);
         const int64_t col4 = n0 + cs * 16 + 4 * (lane >> 4);
         if (row < M) {
-          const uint32_t lo = bf16_rne(acc[t][0]) | (bf16_rne(acc[t][1]) << 16);
-          const uint32_t hi = bf16_rne(acc[t][2]) | (bf16_rne(acc[t][3]) << 16);
+          const uint32_t lo = bf16_out(acc[t][0]) | (bf16_out(acc[t][1]) << 16);
+          const uint32_t hi = bf16_out(acc[t][2]) | (bf16_out(acc[t][3]) << 16);
           *reinterpret_cast<uint2*>(c + row * N + col4) = make_uint2(lo, hi);
         }
       } else {
@@ -1131,7 +1132,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_kernel(const uint8_t*
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int64_t row = i * 16 + 4 * (lane >> 4) + rr;
-          if (row < M) c[row * N + col] = (uint16_t)bf16_rne(acc[t][rr]);
+          if (row < M) c[row * N + col] = (uint16_t)bf16_out(acc[t][rr]);
         }
       }
     }
@@ -1378,7 +1379,7 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_nt_split_kernel(const ui
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int64_t row = e_row[j];
-    if (row < M) c[row * N + n0 + e_col[j]] = (uint16_t)bf16_rne(acc[j]);
+    if (row < M) c[row * N + n0 + e_col[j]] = (uint16_t)bf16_out(acc[j]);
   }
 }
 

@@ -22,7 +22,8 @@ import re
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SOURCES = ["fp8_block_scaled_03_amd/csrc/gemm.hip", "fp8_block_scaled_03_amd/csrc/common.hpp"]
+GEMM_SOURCES = ["fp8_block_scaled_03_amd/csrc/gemm.hip", "fp8_block_scaled_03_amd/csrc/common.hpp",
+                "fp8_block_scaled_03_amd/csrc/launch.hpp"]
 
 
 def _code_only(text: str) -> str:
@@ -34,7 +35,11 @@ def _code_only(text: str) -> str:
 
 
 def source_sha(paths=GEMM_SOURCES) -> str:
+    """Hash of the listed sources (code only) and of the compiler flags every
+    HIP source is built with: a change to either retires a profile."""
+    from . import build
     h = hashlib.sha256()
+    h.update(" ".join(build.COMMON_FLAGS).encode())
     for p in paths:
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())

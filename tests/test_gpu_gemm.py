@@ -2,11 +2,13 @@
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
+import fp8_block_scaled_03_amd as fp8bs
 from fp8_block_scaled_03_amd import workloads as W
 
-from gpu_util import bits_to_f64, gpu_gemm, gpu_grouped, say
+from gpu_util import bits_np, bits_to_f64, f32_dev, gpu_gemm, gpu_grouped, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +124,35 @@ def test_zero_blocks_and_empty_k():
     c = gpu_grouped(np.zeros((96, 0), np.uint8), np.zeros((3, 0), np.float32), np.zeros((3, 0, 64), np.uint8),
                     np.zeros((3, 0, 2), np.float32), off)
     assert c.shape == (96, 64) and np.all(c == 0)
+
+
+def test_zero_results_are_plus_zero_in_every_kernel():
+    """Outputs whose promotions all underflow to a signed zero: an odd number
+    of K-blocks (the tile kernel pairs the last one with a zero-scale block,
+    the small-M kernels do not), scale products far below the fp32 normal
+    range, negative or zero partials.  Every kernel stores such a result as +0,
+    so rows agree bitwise between M = 1, M = 40 and M = 65, and between the
+    [K, N] and K-major entry points."""
+    M, N, K = 65, 64, 96
+    qa = np.zeros((M, K), np.uint8)
+    qb = np.zeros((K, N), np.uint8)
+    qa[:, [0, 32, 64]] = 0x81        # -2^-9 in every K-block
+    qa[1::2, [0, 32, 64]] = 0x80     # -0 codes on odd rows
+    qb[[0, 32, 64], :] = 0x01        # +2^-9
+    qb[[0, 32, 64], 1::3] = 0x81     # -2^-9 in some columns
+    sa = np.full((3, 3), 2.0 ** -70, np.float32)
+    sb = np.full((3, 2), 2.0 ** -70, np.float32)   # s = 2^-140: every product 2^-158 rounds to a zero
+    say("gemm signed-zero results, tile kernel")
+    full = gpu_gemm(qa, sa, qb, sb)
+    assert np.all(full == 0x0000), "zero results stored as +0"
+    for m in (1, 40):
+        say(f"gemm signed-zero results, M={m}")
+        assert np.array_equal(gpu_gemm(qa[:m], sa[:-(-m // 32)], qb, sb), full[:m]), m
+    say("gemm_nt signed-zero results")
+    c_nt = fp8bs.gemm_nt(u8_dev(qa), f32_dev(sa), u8_dev(np.ascontiguousarray(qb.T)),
+                         f32_dev(np.ascontiguousarray(sb.T)))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_np(c_nt), full)
 
 
 def test_rows_independent_of_batch():

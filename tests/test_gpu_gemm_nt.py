@@ -10,6 +10,7 @@ import oracle
 import fp8_block_scaled_03_amd as fp8bs
 from fp8_block_scaled_03_amd import workloads as W
 
+import fullsize_util as FU
 from gpu_util import DEV, bf16_dev, bits_np, bits_to_f64, f32_dev, gpu_gemm, gpu_grouped, i32_dev, say, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -119,10 +120,10 @@ def test_grouped_nt_matches_oracle_and_kn_path(K):
     assert np.array_equal(c, gpu_grouped(qa, sa, qb, sb, off))
 
 
-def test_decode_nt_full_size_sampled():
+def test_decode_nt_full_size():
     """Decode shapes, K = 8192, M = 64 and prefixes: the K-major kernel at full
-    size, sampled blocks against the oracle, every row bitwise equal to the
-    [K, N] kernel's."""
+    size, every element against the oracle and bitwise equal to the [K, N]
+    kernel's, prefixes bitwise equal to the M = 64 rows."""
     for N in (8192, 28672):
         wl = W.decode(64, N)
         a_bits, b_bits = wl.a_bits(), wl.b_bits()
@@ -140,21 +141,19 @@ def test_decode_nt_full_size_sampled():
             cm = fp8bs.gemm_nt(qa[:m].contiguous(), sa[:(m + 31) // 32].contiguous(), qbt, sbt)
             torch.cuda.synchronize()
             assert torch.equal(cm.view(torch.int16), c_nt[:m].view(torch.int16)), f"N={N} M={m}"
-        rng = np.random.default_rng(N)
-        for cb in (0, N // 32 - 1, int(rng.integers(0, N // 32))):
-            cols = slice(cb * 32, cb * 32 + 32)
-            qa_o, sa_o = oracle.quantize_blocks(a_bits)
-            qbt_o, sbt_o = oracle.quantize_blocks(bt_bits[cols])
-            assert np.array_equal(qbt[cols].cpu().numpy(), qbt_o)
-            ref, absref = oracle.gemm_ref_nt(qa_o, sa_o, qbt_o, sbt_o)
-            _assert_tol(bits_np(c_nt[:, cols].contiguous()), ref, absref, f"decode nt N={N} block {cb}")
+        say(f"decode nt N={N}: oracle")
+        qa_o, sa_o = FU.quantize_full(a_bits)
+        qbt_o, sbt_o = FU.quantize_full(bt_bits)
+        FU.assert_same_codes(qbt.cpu().numpy(), sbt.cpu().numpy(), qbt_o, sbt_o, f"decode nt N={N} weight")
+        FU.check_c_full(bits_np(c_nt), FU.dequantize_full(qa_o, sa_o), bt_deq=FU.dequantize_full(qbt_o, sbt_o),
+                        label=f"decode nt N={N}")
         del qa, sa, qbt, sbt, qb, sb, c_nt, c_kn
         torch.cuda.empty_cache()
 
 
-def test_prefill_nt_full_size_sampled():
-    """Prefill M = K = 8192, N = 28672 with the weight K-major: sampled output
-    blocks against the oracle (which quantizes the slabs itself)."""
+def test_prefill_nt_full_size():
+    """Prefill M = K = 8192, N = 28672 with the weight K-major: every element
+    against the oracle (which quantizes both operands itself)."""
     wl = W.prefill(28672)
     a_bits = wl.a_bits()
     bt_bits = np.ascontiguousarray(wl.b_bits().T)
@@ -163,11 +162,14 @@ def test_prefill_nt_full_size_sampled():
     qbt, sbt = fp8bs.quantize(bf16_dev(bt_bits))
     c = fp8bs.gemm_nt(qa, sa, qbt, sbt)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    for rb in (0, 255, int(rng.integers(0, 256))):
-        for cb in (0, 895, int(rng.integers(0, 896))):
-            rows, cols = slice(rb * 32, rb * 32 + 32), slice(cb * 32, cb * 32 + 32)
-            qa_o, sa_o = oracle.quantize_blocks(a_bits[rows])
-            qbt_o, sbt_o = oracle.quantize_blocks(bt_bits[cols])
-            ref, absref = oracle.gemm_ref_nt(qa_o, sa_o, qbt_o, sbt_o)
-            _assert_tol(bits_np(c[rows, cols].contiguous()), ref, absref, f"prefill nt block ({rb},{cb})")
+    c_host = bits_np(c)
+    del c
+    say("prefill nt N=28672: oracle")
+    qa_o, sa_o = FU.quantize_full(a_bits)
+    FU.assert_same_codes(qa.cpu().numpy(), sa.cpu().numpy(), qa_o, sa_o, "prefill nt A")
+    qbt_o, sbt_o = FU.quantize_full(bt_bits)
+    FU.assert_same_codes(qbt.cpu().numpy(), sbt.cpu().numpy(), qbt_o, sbt_o, "prefill nt weight")
+    del qa, sa, qbt, sbt
+    torch.cuda.empty_cache()
+    FU.check_c_full(c_host, FU.dequantize_full(qa_o, sa_o), bt_deq=FU.dequantize_full(qbt_o, sbt_o),
+                    label="prefill nt N=28672")

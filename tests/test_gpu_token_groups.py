@@ -12,6 +12,7 @@ import oracle
 import fp8_block_scaled_03_amd as fp8bs
 from fp8_block_scaled_03_amd import workloads as W
 
+import fullsize_util as FU
 from gpu_util import bf16_dev, bits_np, bits_to_f64, f32_dev, say, u8_dev
 
 pytestmark = pytest.mark.gpu
@@ -130,10 +131,11 @@ def test_chain_is_batch_invariant_end_to_end(k_major):
         assert np.array_equal(gpu_gemm_tg(q1, s1, w, sw, k_major), full[lo:hi]), (lo, hi)
 
 
-def test_decode_and_prefill_tg_full_size_sampled():
+def test_decode_and_prefill_tg_full_size():
     """Decode K = 8192 (M = 64 and prefixes, both N, K-major weight) and
-    prefill M = K = 8192, N = 10240 ([K, N] weight): sampled output blocks
-    against the oracle, which quantizes the slabs itself."""
+    prefill M = K = 8192, N = 10240 ([K, N] weight): every code and scale of A
+    bit-exact, every element of C against the oracle, which quantizes both
+    operands itself."""
     for N in (8192, 28672):
         wl = W.decode(64, N)
         a_bits, b_bits = wl.a_bits(), wl.b_bits()
@@ -147,13 +149,11 @@ def test_decode_and_prefill_tg_full_size_sampled():
             cm = fp8bs.gemm_tg_nt(qa[:m].contiguous(), sa[:m].contiguous(), qbt, sbt)
             torch.cuda.synchronize()
             assert torch.equal(cm.view(torch.int16), c[:m].view(torch.int16)), f"N={N} M={m}"
-        qa_o, sa_o = oracle.quantize_token_groups(a_bits)
-        for cb in (0, N // 32 - 1, 77):
-            cols = slice(cb * 32, cb * 32 + 32)
-            qbt_o, sbt_o = oracle.quantize_blocks(bt_bits[cols])
-            ref, absref = oracle.gemm_ref_tg_nt(qa_o, sa_o, qbt_o, sbt_o)
-            ok = oracle.tolerance_ok(bits_to_f64(bits_np(c[:, cols].contiguous())), ref, absref)
-            assert ok.all(), f"decode tg N={N} block {cb}"
+        qa_o, sa_o = FU.quantize_full(a_bits, token_groups=True)
+        FU.assert_same_codes(qa.cpu().numpy(), sa.cpu().numpy(), qa_o, sa_o, f"decode tg N={N} A")
+        qbt_o, sbt_o = FU.quantize_full(bt_bits)
+        FU.check_c_full(bits_np(c), FU.dequantize_full(qa_o, sa_o, token_groups=True),
+                        bt_deq=FU.dequantize_full(qbt_o, sbt_o), label=f"decode tg N={N}")
         del qa, sa, qbt, sbt, c
         torch.cuda.empty_cache()
     wl = W.prefill(10240)
@@ -163,12 +163,11 @@ def test_decode_and_prefill_tg_full_size_sampled():
     qb, sb = fp8bs.quantize(bf16_dev(b_bits))
     c = fp8bs.gemm_tg(qa, sa, qb, sb)
     torch.cuda.synchronize()
-    for rb in (0, 255, 101):
-        rows = slice(rb * 32, rb * 32 + 32)
-        qa_o, sa_o = oracle.quantize_token_groups(a_bits[rows])
-        for cb in (0, 319, 150):
-            cols = slice(cb * 32, cb * 32 + 32)
-            qb_o, sb_o = oracle.quantize_blocks(np.ascontiguousarray(b_bits[:, cols]))
-            ref, absref = oracle.gemm_ref_tg(qa_o, sa_o, qb_o, sb_o)
-            ok = oracle.tolerance_ok(bits_to_f64(bits_np(c[rows, cols].contiguous())), ref, absref)
-            assert ok.all(), f"prefill tg block ({rb},{cb})"
+    c_host = bits_np(c)
+    qa_o, sa_o = FU.quantize_full(a_bits, token_groups=True)
+    FU.assert_same_codes(qa.cpu().numpy(), sa.cpu().numpy(), qa_o, sa_o, "prefill tg A")
+    qb_o, sb_o = FU.quantize_full(b_bits)
+    del qa, sa, qb, sb, c
+    torch.cuda.empty_cache()
+    FU.check_c_full(c_host, FU.dequantize_full(qa_o, sa_o, token_groups=True), FU.dequantize_full(qb_o, sb_o),
+                    label="prefill tg N=10240")
