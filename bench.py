@@ -86,9 +86,11 @@ def main():
 
     import torch
     import fp8_block_scaled_03_amd as fp8bs
+    from fp8_block_scaled_03_amd import probe
     from fp8_block_scaled_03_amd import workloads as W
 
     fp8bs.load_library()  # fail loudly before any work if the library is missing
+    probe.load_probe_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -127,15 +129,18 @@ def main():
             dec_w[(n_dec, kind)][2] = True
         return q, sc
 
-    # Cache flush between timed launches: READ 1 GiB (written once, here).  A
-    # read evicts L2 and the 256 MB Infinity Cache and leaves only clean lines;
-    # a write flush would leave dirty lines whose write-back then runs inside
-    # the next timed launch and halves the bandwidth it sees.
+    # Cache flush between timed launches: READ 1 GiB (written once, here) with
+    # the probe library's streaming read.  A read evicts L2 and the 256 MB
+    # Infinity Cache and leaves only clean lines; a write flush would leave
+    # dirty lines whose write-back then runs inside the next timed launch and
+    # halves the bandwidth it sees.
     flush_buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    FLUSH_WG = 256                      # one workgroup per CU read 1 GiB fastest
+    flush_out = torch.empty(8 * 2048, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     def flush():
-        flush_buf.max()  # a read-only reduction (sum would first widen to an int64 copy)
+        probe.stream_read(flush_buf, flush_out[:8 * FLUSH_WG], FLUSH_WG)
 
     def time_launch(fn, reps, do_flush=True):
         """Median and min per-launch time in ms, HIP events on the launch stream."""
@@ -307,11 +312,28 @@ def main():
     def ms_entry(med, mn):
         return {"median": round(med, 5), "min": round(mn, 5)}
 
-    # streaming-read ceiling of this GPU in this run: the cache flush itself
-    # (a read of 1 GiB)
+    # streaming-read ceilings of this GPU in this run: the 1 GiB flush read
+    # itself, and a plain read of a decode weight's byte count after a flush
     flush()
     fl_med, fl_min, _ = time_launch(flush, 10, do_flush=False)
     stream_gbs = flush_buf.numel() * 4 / (fl_med * 1e-3) / 1e9
+
+    def stream_ceiling(nbytes):
+        """GB/s of a plain read of nbytes (a view of the flush buffer) with cold caches."""
+        view = flush_buf[: nbytes // 4]
+        best = None
+        for wg in (512, 1024, 2048):
+            med, _, _ = time_launch(lambda: probe.stream_read(view, flush_out[:8 * wg], wg), 10)
+            best = med if best is None else min(best, med)
+        return nbytes / (best * 1e-3) / 1e9
+
+    # the exact recipe's instruction-mix ceiling (one 16x16x32 bf16 MFMA and
+    # four fp32 FMAs per step, registers only), four waves per SIMD
+    pc_wg, pc_iters = 1024, 2000
+    pc_out = torch.empty(pc_wg * 8, dtype=torch.float32, device=dev)
+    probe.promote_ceiling(pc_out, pc_wg, 200)
+    pc_med, _, _ = time_launch(lambda: probe.promote_ceiling(pc_out, pc_wg, pc_iters), 5, do_flush=False)
+    promote_ceiling_tflops = pc_wg * 8 * pc_iters * 8 * probe.PROMOTE_CEILING_FLOPS_PER_STEP / (pc_med * 1e-3) / 1e12
 
     for _ in range(5):
         gemm_only()
@@ -328,7 +350,12 @@ def main():
         "quantize_4096x4096_ms": ms_entry(q_med, q_min),
         "quantize_4096x4096_gbs": round(3.0 * M * K / (q_med * 1e-3) / 1e9, 1),
         "stream_read_ceiling": {"gbs": round(stream_gbs, 1), "frac_hbm_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
-                                "what": "the 1 GiB cache-flush read (a max reduction), median of 10"},
+                                "what": "the 1 GiB cache-flush read (probe streaming read), median of 10"},
+        "promote_ceiling": {"tflops": round(promote_ceiling_tflops, 1),
+                            "frac_fp8_peak": round(promote_ceiling_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
+                            "gemm_in_step_frac_of_it": round(achieved / promote_ceiling_tflops, 4),
+                            "what": "registers-only loop of one 16x16x32 bf16 MFMA + four fp32 FMAs per step, "
+                                    "8192 waves (4 per SIMD)"},
     }
 
     # square 256^3 (quantize both operands + GEMM, and the GEMM alone): a
@@ -348,11 +375,15 @@ def main():
                             "step_us": {"median": round(ss_med * 1e3, 2), "min": round(ss_min * 1e3, 2)}}
     del s_a, s_b, s_qa, s_sa, s_qb, s_sb, s_c
 
+    weight_ceiling = {}
+
     def decode_entry(m, n_dec, k, nbytes, d_med, d_min):
         gbs = nbytes / (d_med * 1e-3) / 1e9
+        if n_dec not in weight_ceiling:
+            weight_ceiling[n_dec] = stream_ceiling(k * n_dec)
         return {"M": m, "N": n_dec, "K": k, "median_us": round(d_med * 1e3, 2), "min_us": round(d_min * 1e3, 2),
                 "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                "frac_stream_read": round(gbs / stream_gbs, 4)}
+                "frac_stream_read": round(gbs / weight_ceiling[n_dec], 4)}
 
     if not args.quick:
         def decode_sweep(k_major, token_groups):
@@ -381,6 +412,11 @@ def main():
             return rows_out
 
         detail["decode_small_m"] = decode_sweep(False, False)
+        detail["stream_read_ceiling"]["weight_gbs"] = {
+            str(n): round(v, 1) for n, v in weight_ceiling.items()}
+        detail["stream_read_ceiling"]["weight_what"] = ("a plain read of the decode weight's byte count (K x N) "
+                                                        "after a flush, best of 512 / 1024 / 2048 workgroups; "
+                                                        "the rows' frac_stream_read is against it")
         # the weight K-major (B^T [N, K], the layout of the pages' call
         # interface): each workgroup streams whole weight rows
         detail["decode_small_m_k_major_weight"] = decode_sweep(True, False)

@@ -34,7 +34,8 @@ from .gemm import (dequantize, dequantize_token_groups, gemm_ref, gemm_ref_at, g
                    tolerance_bound, bf16_bits_to_f64)
 from .exact import gemm_exact
 from .rmsnorm import residual_add, rmsnorm_ref, rmsnorm_tolerance_ok, RMS_REL_TOL, RMS_ABS_TOL
-from .e8m0 import e8m0_exponent, quantize_blocks_e8m0, dequantize_e8m0, gemm_ref_e8m0_nt
+from .e8m0 import (e8m0_exponent, quantize_blocks_e8m0, dequantize_e8m0, gemm_ref_e8m0_nt, gemm_e8m0_bound_nt,
+                   emulate_gemm_e8m0_nt)
 
 __all__ = [
     "Minifloat", "E4M3FN", "FP16", "BF16",
@@ -46,5 +47,6 @@ __all__ = [
     "tolerance_ok", "tolerance_bound", "bf16_bits_to_f64",
     "gemm_exact",
     "residual_add", "rmsnorm_ref", "rmsnorm_tolerance_ok", "RMS_REL_TOL", "RMS_ABS_TOL",
-    "e8m0_exponent", "quantize_blocks_e8m0", "dequantize_e8m0", "gemm_ref_e8m0_nt",
+    "e8m0_exponent", "quantize_blocks_e8m0", "dequantize_e8m0", "gemm_ref_e8m0_nt", "gemm_e8m0_bound_nt",
+    "emulate_gemm_e8m0_nt",
 ]

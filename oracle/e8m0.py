@@ -16,6 +16,22 @@ pages describe no such variant; the readings taken:
 
 GEMM: C[i, j] = sum_k dec(A[i, k]) 2**Ea[i//32, k//32] * dec(Bt[j, k]) 2**Eb[j//32, k//32],
 the plain definition, with the weight K-major (Bt [N, K]).
+
+Error bound of a GEMM that sums 128 K at a time in one instruction
+(``gemm_e8m0_bound_nt``).  The pages do not describe such an instruction;
+the bound follows a stated model of how a 128-deep FP8 step with per-32-K
+power-of-two scales sums its terms:
+
+* the 128 products of a step fall into 16 groups of 8 consecutive K;
+* the exponent sum of a product is S = x(a) + x(b) + Ea + Eb, where x(c) is
+  the exponent of code c with its significand read in [0, 2) (E - 7 for a
+  normal code, -6 for a subnormal code or zero);
+* first stage: every product of group g is cut toward zero to a multiple of
+  2**(S_g - 13), S_g the largest S in the group;
+* later stages (groups, blocks of 32, the accumulator input): each group's
+  contribution, and the accumulator input, may lose at most 2**(S_max - 23),
+  S_max the largest S of the step or the accumulator input's exponent;
+* the step's result is rounded to fp32, nearest even.
 """
 
 from __future__ import annotations
@@ -87,3 +103,182 @@ def gemm_ref_e8m0_nt(qa, ea, qbt, ebt):
     a = dequantize_e8m0(qa, ea)
     bt = dequantize_e8m0(qbt, ebt)
     return a @ bt.T, np.abs(a) @ np.abs(bt).T
+
+
+# ---- the summation model of a 128-deep scaled FP8 step, and the bound it implies ----
+STEP_K = 128           # K per step
+GROUP = 8              # products summed together in the first stage
+GROUP_GRID_BITS = 13   # first stage: cut toward zero to a multiple of 2**(S_g - 13)
+LATER_LOSS_BITS = 23   # later stages: at most 2**(S_max - 23) per group and for the accumulator input
+
+
+def code_exponents(q):
+    """x(c): the exponent of each E4M3 code with its significand read in
+    [0, 2) - E - 7 for a normal code, -6 for a subnormal code and for zero."""
+    E = (np.asarray(q, dtype=np.int64) >> 3) & 15
+    return np.maximum(E, 1) - 7
+
+
+def step_bound(absp, S, c_abs):
+    """Bound on |computed - exact| of one step under the model.
+
+    absp  [..., 128] |products| (fp64, exact);
+    S     [..., 128] their exponent sums (integers; zero products included, so
+          that a group's and a step's largest S are never underestimated);
+    c_abs [...]      an upper bound on |accumulator input|.
+    Returns (loss of the summation stages, the fp32 rounding's half-ulp factor
+    is applied by the caller)."""
+    absp = np.asarray(absp, dtype=np.float64)
+    S = np.asarray(S, dtype=np.int64)
+    lead = absp.shape[:-1]
+    ng = absp.shape[-1] // GROUP
+    pg = absp.reshape(*lead, ng, GROUP)
+    Sg = S.reshape(*lead, ng, GROUP).max(axis=-1)                        # [..., ng]
+    grid = np.ldexp(1.0, Sg - GROUP_GRID_BITS)[..., None]                 # exact powers of two
+    first = (pg - np.floor(pg / grid) * grid).sum(axis=(-2, -1))         # exact remainders, summed
+    c_abs = np.asarray(c_abs, dtype=np.float64)
+    c_exp = np.where(c_abs > 0, np.floor(np.log2(np.where(c_abs > 0, c_abs, 1.0))), -10 ** 6).astype(np.int64)
+    s_max = np.maximum(Sg.max(axis=-1), c_exp)
+    env = np.ldexp(1.0, s_max - LATER_LOSS_BITS)
+    later = np.minimum(pg.sum(axis=-1), env[..., None]).sum(axis=-1) + np.minimum(c_abs, env)
+    return first + later
+
+
+def gemm_e8m0_bound_nt(qa, ea, qbt, ebt, bf16_out=True):
+    """Reference and per-element error bound for a GEMM that runs the model's
+    steps over K in ascending order (accumulator starts at +0) and rounds the
+    fp32 result to bf16, nearest even (bf16_out=False: the bound of the fp32
+    result before that rounding).
+
+    Returns (ref, bound): the fp64 product, and B such that the model's bf16
+    output satisfies |C - ref| <= B.  Per step t: the summation loss of
+    ``step_bound`` with the accumulator input bounded by U_{t-1}, plus half an
+    fp32 ulp of the step's result (2**-24 * U_t, plus 2**-150 for a
+    subnormal); U_t = |exact prefix| + the bound so far.  At the end half a
+    bf16 ulp of the result (2**-8 * (|ref| + B), plus 2**-134)."""
+    qa = np.asarray(qa, dtype=np.uint8)
+    qbt = np.asarray(qbt, dtype=np.uint8)
+    M, K = qa.shape
+    N = qbt.shape[0]
+    if K % STEP_K:
+        raise ValueError("K must be a multiple of 128")
+    a = dequantize_e8m0(qa, ea)
+    bt = dequantize_e8m0(qbt, ebt)
+    xa = code_exponents(qa) + np.repeat(np.repeat(np.asarray(ea, np.int64) - 127, BLOCK, 0)[:M], BLOCK, 1)
+    xb = code_exponents(qbt) + np.repeat(np.repeat(np.asarray(ebt, np.int64) - 127, BLOCK, 0)[:N], BLOCK, 1)
+    prefix = np.zeros((M, N))
+    prefix_abs = np.zeros((M, N))
+    B = np.zeros((M, N))
+    for k0 in range(0, K, STEP_K):
+        ks = slice(k0, k0 + STEP_K)
+        absp = np.abs(a[:, None, ks]) * np.abs(bt[None, :, ks])            # [M, N, 128], exact
+        S = xa[:, None, ks] + xb[None, :, ks]
+        c_abs = np.abs(prefix) + 2.0 ** -40 * prefix_abs + B
+        loss = step_bound(absp, S, c_abs)
+        prefix = prefix + a[:, ks] @ bt[:, ks].T
+        prefix_abs = prefix_abs + absp.sum(axis=-1)
+        U = np.abs(prefix) + 2.0 ** -40 * prefix_abs + B + loss
+        B = B + loss + 2.0 ** -24 * U + 2.0 ** -150
+    ref = prefix
+    bound = B + 2.0 ** -8 * (np.abs(ref) + B) + 2.0 ** -134 if bf16_out else B
+    # the bound itself is formed in fp64 (a few hundred roundings of 2**-53)
+    return ref, bound * (1.0 + 2.0 ** -30)
+
+
+def _fp32_rne(x):
+    """Fraction -> nearest fp32 value (ties to even), as a Fraction (finite range)."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    ax = abs(x)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    while Fraction(2) ** e > ax:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= ax:
+        e += 1
+    unit = Fraction(2) ** max(e - 23, -149)
+    n = ax / unit
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return (1 if x > 0 else -1) * fl * unit
+
+
+def _bf16_rne(x):
+    """Fraction (an fp32 value) -> nearest bf16 value (ties to even), as a Fraction."""
+    from fractions import Fraction
+    if x == 0:
+        return Fraction(0)
+    ax = abs(x)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    while Fraction(2) ** e > ax:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= ax:
+        e += 1
+    unit = Fraction(2) ** max(e - 7, -133)
+    n = ax / unit
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return (1 if x > 0 else -1) * fl * unit
+
+
+def emulate_gemm_e8m0_nt(qa, ea, qbt, ebt, later="exact", bf16_out=True):
+    """Brute-force emulation of the summation model, exact rationals (tiny
+    shapes only).  The first stage is the model's (cut toward zero per product
+    within each group of 8); `later` picks one behaviour of the later stages,
+    each within the model's 2**(S_max - 23) per group:
+      "exact" - group sums and the accumulator input added exactly;
+      "grid"  - each group sum and the accumulator input cut toward zero to a
+                multiple of 2**(S_max - 24);
+      "drop"  - groups whose largest S is below S_max - 27 left out.
+    Every step's result is rounded to fp32 (nearest even), the last one to
+    bf16 (bf16_out=False: left in fp32).  Returns the outputs as an object
+    array of Fractions."""
+    from fractions import Fraction
+    qa = np.asarray(qa, dtype=np.uint8)
+    qbt = np.asarray(qbt, dtype=np.uint8)
+    M, K = qa.shape
+    N = qbt.shape[0]
+    a = dequantize_e8m0(qa, ea)
+    bt = dequantize_e8m0(qbt, ebt)
+    xa = code_exponents(qa) + np.repeat(np.repeat(np.asarray(ea, np.int64) - 127, BLOCK, 0)[:M], BLOCK, 1)
+    xb = code_exponents(qbt) + np.repeat(np.repeat(np.asarray(ebt, np.int64) - 127, BLOCK, 0)[:N], BLOCK, 1)
+
+    def cut(v, grid):
+        n = abs(v) / grid
+        t = (n.numerator // n.denominator) * grid
+        return t if v >= 0 else -t
+
+    out = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            for k0 in range(0, K, STEP_K):
+                groups = []
+                s_max = None
+                for g0 in range(k0, k0 + STEP_K, GROUP):
+                    ks = range(g0, g0 + GROUP)
+                    sg = max(int(xa[i, k] + xb[j, k]) for k in ks)
+                    grid = Fraction(2) ** (sg - GROUP_GRID_BITS)
+                    groups.append((sg, sum((cut(Fraction(float(a[i, k])) * Fraction(float(bt[j, k])), grid)
+                                            for k in ks), Fraction(0))))
+                    s_max = sg if s_max is None else max(s_max, sg)
+                if acc != 0:
+                    ae = abs(acc).numerator.bit_length() - abs(acc).denominator.bit_length()
+                    while Fraction(2) ** ae > abs(acc):
+                        ae -= 1
+                    s_max = max(s_max, ae)
+                total = acc
+                if later == "grid":
+                    g24 = Fraction(2) ** (s_max - 24)
+                    total = cut(acc, g24) + sum((cut(v, g24) for _, v in groups), Fraction(0))
+                elif later == "drop":
+                    total = acc + sum((v for sg, v in groups if sg >= s_max - 27), Fraction(0))
+                else:
+                    total = acc + sum((v for _, v in groups), Fraction(0))
+                acc = _fp32_rne(total)
+            out[i, j] = _bf16_rne(acc) if bf16_out else acc
+    return out

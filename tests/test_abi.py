@@ -30,6 +30,24 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_every_declared_symbol_and_checks_arguments():
+    """libfp8bs_probe.so (measurement and test support) exports what
+    include/fp8bs_probe.h declares and rejects bad sizes before any launch."""
+    from fp8_block_scaled_03_amd import probe
+    lib = probe.load_probe_library()
+    text = open(os.path.join(ROOT, "include", "fp8bs_probe.h")).read()
+    names = sorted(set(re.findall(r"\b(fp8bs_probe_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["fp8bs_probe_gemm", "fp8bs_probe_mfma_scale", "fp8bs_probe_promote_ceiling",
+                     "fp8bs_probe_stream_read"]
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fp8bs_probe_gemm(A16, A4, A16, A4, A16, None, 48, 64, 64, 0, None) == 2     # M % 32
+    assert lib.fp8bs_probe_gemm(None, A4, A16, A4, A16, None, 64, 64, 64, 0, None) == 1
+    assert lib.fp8bs_probe_mfma_scale(A16, A16, A16, A16, A4, A4, 0, None) == 2
+    assert lib.fp8bs_probe_promote_ceiling(None, 1, 1, None) == 1
+    assert lib.fp8bs_probe_stream_read(A16, 24, A4, 1, None) == 2                          # bytes % 16
+
+
 def test_status_strings():
     lib = binding.load_library()
     for code in range(6):
