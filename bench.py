@@ -355,7 +355,7 @@ def main():
                             "frac_fp8_peak": round(promote_ceiling_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
                             "gemm_in_step_frac_of_it": round(achieved / promote_ceiling_tflops, 4),
                             "what": "registers-only loop of one 16x16x32 bf16 MFMA + four fp32 FMAs per step, "
-                                    "8192 waves (4 per SIMD)"},
+                                    "1024 workgroups of eight waves (up to 8 waves per SIMD)"},
     }
 
     # square 256^3 (quantize both operands + GEMM, and the GEMM alone): a

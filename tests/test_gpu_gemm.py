@@ -244,6 +244,31 @@ def test_grouped_all_empty_but_one_and_untouched_rows():
     _assert_tol(c, ref, absref, "grouped one live group")
 
 
+def test_grouped_many_groups_heavy_and_light_tiles():
+    """130 groups (the tile lookup walks the offsets 64 groups at a time) with
+    sizes from 0 to 544 rows in 32-row steps: full 256-row tiles, tails above
+    and at most 128 rows, empty groups.  Every group's rows equal a single
+    GEMM on them, bitwise, and the whole output is within the bound."""
+    G, K, N = 130, 96, 64
+    g = np.random.default_rng(77)
+    rows = 32 * g.integers(0, 18, G)
+    rows[[3, 64, 65, 129]] = 0
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
+    M = int(off[-1])
+    qa, sa = _quantized(70, M, K)
+    qb = np.stack([_quantized(1000 + i, K, N, std=0.02)[0] for i in range(G)])
+    sb = np.stack([_quantized(1000 + i, K, N, std=0.02)[1] for i in range(G)])
+    say(f"grouped G={G} M={M}")
+    c = gpu_grouped(qa, sa, qb, sb, off)
+    ref, absref = oracle.grouped_gemm_ref(qa, sa, qb, sb, off)
+    _assert_tol(c, ref, absref, "grouped many groups")
+    for gi in (0, 1, 63, 66, 100, 128):
+        r0, r1 = int(off[gi]), int(off[gi + 1])
+        if r1 > r0:
+            say(f"grouped many groups: group {gi} as a single GEMM")
+            assert np.array_equal(c[r0:r1], gpu_gemm(qa[r0:r1], sa[r0 // 32:r1 // 32], qb[gi], sb[gi])), gi
+
+
 def _effective_ranges(off, M_total):
     """The documented treatment of a bad offsets table: each range clipped to
     [0, M_total], started no earlier than the previous range's end, and empty
