@@ -328,12 +328,18 @@ def main():
         return nbytes / (best * 1e-3) / 1e9
 
     # the exact recipe's instruction-mix ceiling (one 16x16x32 bf16 MFMA and
-    # four fp32 FMAs per step, registers only), four waves per SIMD
-    pc_wg, pc_iters = 1024, 2000
+    # four fp32 FMAs per step, registers only), and the same steps' MFMAs alone
+    # and FMAs alone: on gfx950 the mix takes about the sum of the two
+    pc_wg, pc_iters = 512, 4000
     pc_out = torch.empty(pc_wg * 8, dtype=torch.float32, device=dev)
-    probe.promote_ceiling(pc_out, pc_wg, 200)
-    pc_med, _, _ = time_launch(lambda: probe.promote_ceiling(pc_out, pc_wg, pc_iters), 5, do_flush=False)
-    promote_ceiling_tflops = pc_wg * 8 * pc_iters * 8 * probe.PROMOTE_CEILING_FLOPS_PER_STEP / (pc_med * 1e-3) / 1e12
+    pc_us = {}
+    for mode in (0, 1, 2, 3):
+        probe.promote_ceiling(pc_out, pc_wg, 200, mode)
+        med, _, _ = time_launch(lambda mode=mode: probe.promote_ceiling(pc_out, pc_wg, pc_iters, mode), 5,
+                                do_flush=False)
+        pc_us[mode] = med * 1e3
+    promote_ceiling_tflops = (pc_wg * 8 * pc_iters * 8 * probe.PROMOTE_CEILING_FLOPS_PER_STEP
+                              / (pc_us[0] * 1e-6) / 1e12)
 
     for _ in range(5):
         gemm_only()
@@ -354,8 +360,11 @@ def main():
         "promote_ceiling": {"tflops": round(promote_ceiling_tflops, 1),
                             "frac_fp8_peak": round(promote_ceiling_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
                             "gemm_in_step_frac_of_it": round(achieved / promote_ceiling_tflops, 4),
+                            "us_mix_mfma_only_fma_only_fp8mfma_only": [round(pc_us[m], 1) for m in (0, 1, 2, 3)],
                             "what": "registers-only loop of one 16x16x32 bf16 MFMA + four fp32 FMAs per step, "
-                                    "1024 workgroups of eight waves (up to 8 waves per SIMD)"},
+                                    "512 workgroups of eight waves (4 waves per SIMD); also the same "
+                                    "steps with the MFMAs alone, with the FMAs alone, and with the FP8 form of "
+                                    "the MFMA alone"},
     }
 
     # square 256^3 (quantize both operands + GEMM, and the GEMM alone): a

@@ -112,39 +112,60 @@ __global__ void __launch_bounds__(64) probe_mfma_scale_kernel(const uint8_t* __r
 // The exact recipe's instruction mix, registers only: per step one
 // v_mfma_f32_16x16x32_bf16 with a zero accumulator input, and four fp32 FMAs
 // that promote the partial formed RING steps earlier (so they never wait on
-// the MFMA just issued).  Operands are rotated through the loop so nothing is
-// invariant.  Each wave writes one value so nothing is dead.
+// the MFMA just issued).  MODE 1 keeps only the MFMAs, MODE 2 only the FMAs
+// (the same count, on partials that are left as they were), so the three
+// rates show how far the two kinds of work overlap on one SIMD; MODE 3 runs
+// v_mfma_f32_16x16x32_fp8_fp8 alone instead of the bf16 form.  The eight
+// steps of an iteration use eight different A operands and a B operand that
+// is rotated every iteration, so no two MFMAs are alike and none is loop
+// invariant; every MFMA result is read (by the FMAs, or by the final sum
+// through its own slot), and each wave writes one value, so nothing is dead.
 constexpr int RING = 4;
+template <int MODE>
 __global__ void __launch_bounds__(512) probe_promote_ceiling_kernel(float* __restrict__ out, int iters, float seed) {
   const int lane = threadIdx.x & 63;
-  v8bf a, b;
+  v8bf a[8], b;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)(seed * (float)(lane + e + 1));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u][e] = (__bf16)(seed * (float)(lane + e + 3 * u + 1));
     b[e] = (__bf16)(seed * (float)(lane - e + 3));
   }
   v4f acc[4];
-  v4f ring[RING];
+  v4f ring[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < RING; ++i) ring[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < 8; ++i) ring[i] = v4f{seed, seed, seed, seed};
   float s = seed;
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const v4f p = mfma_partial(u & 1 ? b : a, u & 1 ? a : b);
-      promote(acc[u & 3], ring[u % RING], s);
-      ring[u % RING] = p;
+      if constexpr (MODE == 0) {
+        const v4f p = mfma_partial(a[u], b);
+        promote(acc[u & 3], ring[u % RING], s);
+        ring[u % RING] = p;
+      } else if constexpr (MODE == 1) {
+        ring[u] = mfma_partial(a[u], b);
+      } else if constexpr (MODE == 2) {
+        promote(acc[u & 3], ring[u % RING], s);
+      } else {
+        // the FP8 form of a 32-deep partial, on the operands' raw bits
+        const v4i ai = __builtin_bit_cast(v4i, a[u]), bi = __builtin_bit_cast(v4i, b);
+        const long a8 = ((long)ai[0] << 32) | (unsigned)ai[1];
+        const long b8 = ((long)bi[2] << 32) | (unsigned)bi[3];
+        ring[u] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, z, 0, 0, 0);
+      }
     }
     s = s * 0.999f;
-    a = __builtin_shufflevector(a, a, 1, 2, 3, 4, 5, 6, 7, 0);
+    b = __builtin_shufflevector(b, b, 1, 2, 3, 4, 5, 6, 7, 0);
   }
   float t = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) t += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
 #pragma unroll
-  for (int i = 0; i < RING; ++i) t += ring[i][0];
+  for (int i = 0; i < 8; ++i) t += ring[i][0] + ring[i][1] + ring[i][2] + ring[i][3];
   if (lane == 0) out[(int64_t)blockIdx.x * 8 + (threadIdx.x >> 6)] = t;
 }
 
@@ -203,11 +224,18 @@ int fp8bs_probe_mfma_scale(const void* a, const void* bt, const void* ea, const 
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
-int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, void* stream) {
+int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode, void* stream) {
   if (!out) return 1;
-  if (workgroups <= 0 || iters <= 0) return 2;
-  hipLaunchKernelGGL(probe_promote_ceiling_kernel, dim3((unsigned)workgroups), dim3(512), 0, (hipStream_t)stream,
-                     out, iters, 1.0f / 1024.0f);
+  if (workgroups <= 0 || iters <= 0 || mode < 0 || mode > 3) return 2;
+  const dim3 grid((unsigned)workgroups), block(512);
+  if (mode == 0)
+    hipLaunchKernelGGL(probe_promote_ceiling_kernel<0>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
+  else if (mode == 1)
+    hipLaunchKernelGGL(probe_promote_ceiling_kernel<1>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
+  else if (mode == 2)
+    hipLaunchKernelGGL(probe_promote_ceiling_kernel<2>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
+  else
+    hipLaunchKernelGGL(probe_promote_ceiling_kernel<3>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -31,7 +31,7 @@ def load_probe_library() -> ctypes.CDLL:
         lib.fp8bs_probe_gemm.restype = i32
         lib.fp8bs_probe_mfma_scale.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp]
         lib.fp8bs_probe_mfma_scale.restype = i32
-        lib.fp8bs_probe_promote_ceiling.argtypes = [vp, i32, i32, vp]
+        lib.fp8bs_probe_promote_ceiling.argtypes = [vp, i32, i32, i32, vp]
         lib.fp8bs_probe_promote_ceiling.restype = i32
         lib.fp8bs_probe_stream_read.argtypes = [vp, ctypes.c_longlong, vp, i32, vp]
         lib.fp8bs_probe_stream_read.restype = i32
@@ -77,10 +77,12 @@ def mfma_scale(a, bt, ea, eb, cin):
     return d
 
 
-def promote_ceiling(out, workgroups: int, iters: int):
-    """Enqueue the register-only MFMA + promotion loop (out: fp32 [workgroups * 8])."""
+def promote_ceiling(out, workgroups: int, iters: int, mode: int = 0):
+    """Enqueue the register-only MFMA + promotion loop (out: fp32 [workgroups * 8]);
+    mode 0 = MFMA + four FMAs per step, 1 = the MFMAs alone, 2 = the FMAs alone,
+    3 = the FP8 form of the MFMA alone."""
     rc = load_probe_library().fp8bs_probe_promote_ceiling(
-        _dev(out, torch.float32, (workgroups * 8,), "out"), workgroups, iters, _stream_ptr(out))
+        _dev(out, torch.float32, (workgroups * 8,), "out"), workgroups, iters, mode, _stream_ptr(out))
     _ok(rc, "fp8bs_probe_promote_ceiling")
 
 

@@ -58,10 +58,14 @@ int fp8bs_probe_mfma_scale(const void* a, const void* bt, const void* ea, const 
  * only: one v_mfma_f32_16x16x32_bf16 (16384 flops) and four fp32 FMAs that
  * promote a partial formed four steps earlier [DG 2.2-2.3].  Its rate bounds
  * any kernel that forms every 32-deep partial with that MFMA and promotes it
- * with non-packed fp32 FMAs.  out [workgroups * 8] fp32 (one value per wave,
- * written so that nothing is dead code).  workgroups, iters > 0.
+ * with non-packed fp32 FMAs.  mode 0: that mix; mode 1: the MFMAs alone;
+ * mode 2: the FMAs alone (the same counts), so that the three rates show how
+ * far the two kinds of work overlap; mode 3: v_mfma_f32_16x16x32_fp8_fp8
+ * alone, the FP8 form of the same partial.  out [workgroups * 8] fp32 (one
+ * value per wave, written so that nothing is dead code).  workgroups,
+ * iters > 0, mode in 0..3.
  */
-int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, void* stream);
+int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode, void* stream);
 
 /*
  * fp8bs_probe_stream_read - read `bytes` of `buf` once (16-byte loads,

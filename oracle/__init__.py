@@ -35,7 +35,7 @@ from .gemm import (dequantize, dequantize_token_groups, gemm_ref, gemm_ref_at, g
 from .exact import gemm_exact
 from .rmsnorm import residual_add, rmsnorm_ref, rmsnorm_tolerance_ok, RMS_REL_TOL, RMS_ABS_TOL
 from .e8m0 import (e8m0_exponent, quantize_blocks_e8m0, dequantize_e8m0, gemm_ref_e8m0_nt, gemm_e8m0_bound_nt,
-                   emulate_gemm_e8m0_nt)
+                   emulate_gemm_e8m0_nt, code_exponents, step_bound)
 
 __all__ = [
     "Minifloat", "E4M3FN", "FP16", "BF16",
@@ -48,5 +48,5 @@ __all__ = [
     "gemm_exact",
     "residual_add", "rmsnorm_ref", "rmsnorm_tolerance_ok", "RMS_REL_TOL", "RMS_ABS_TOL",
     "e8m0_exponent", "quantize_blocks_e8m0", "dequantize_e8m0", "gemm_ref_e8m0_nt", "gemm_e8m0_bound_nt",
-    "emulate_gemm_e8m0_nt",
+    "emulate_gemm_e8m0_nt", "code_exponents", "step_bound",
 ]
