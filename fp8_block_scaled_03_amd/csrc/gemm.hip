@@ -144,10 +144,16 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // address instead of zeros: they feed only outputs that are never stored.
   // Unconditional loads let the compiler count them exactly, so the wait before
   // staging covers only the K-block being staged, not the one loaded after it.
-  auto load_stage = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
+  auto load_a_only = [&](int kb, uint4& ra) __attribute__((always_inline)) {
     ra = *reinterpret_cast<const uint4*>(a_src + (int64_t)kb * 32);
+  };
+  auto load_b_only = [&](int kb, uint4& rb) __attribute__((always_inline)) {
     const int64_t boff = BT ? (int64_t)kb * 32 : (int64_t)kb * 32 * N;
     rb = *reinterpret_cast<const uint4*>(b_src + boff);
+  };
+  auto load_stage = [&](int kb, uint4& ra, uint4& rb) __attribute__((always_inline)) {
+    load_a_only(kb, ra);
+    load_b_only(kb, rb);
   };
   // `st` is the stage index (wave-uniform, 0..2)
   auto store_stage = [&](int st, uint4 ra, uint4 rb) __attribute__((always_inline)) {
@@ -161,6 +167,18 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     *(lds_v4u*)(st_a1 + soa) = v4u{a1.x, a1.y, a1.z, a1.w};
     *(lds_v4u*)(st_b + sob) = v4u{b0.x, b0.y, b0.z, b0.w};
     *(lds_v4u*)(st_b1 + sob) = v4u{b1.x, b1.y, b1.z, b1.w};
+  };
+  // One quarter of store_stage: 8 E4M3 bytes (half of ra or rb) -> 8 bf16 ->
+  // one 16-byte LDS store.  piece 0/1: the low/high half of ra (A), 2/3: of rb.
+  auto store_piece = [&](int st, int piece, uint4 ra, uint4 rb) __attribute__((always_inline)) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4u lds_v4u;
+    const uint4 src = piece < 2 ? ra : rb;
+    const uint32_t w0 = (piece & 1) ? src.z : src.x, w1 = (piece & 1) ? src.w : src.y;
+    const v2i x = e4m3x4_to_bf16x4(w0), y = e4m3x4_to_bf16x4(w1);
+    lds_u8* dst = piece == 0 ? st_a0 + st * A_STAGE_BYTES : piece == 1 ? st_a1 + st * A_STAGE_BYTES
+                : piece == 2 ? st_b + st * B_STAGE_BYTES : st_b1 + st * B_STAGE_BYTES;
+    *(lds_v4u*)dst = v4u{(unsigned)x[0], (unsigned)x[1], (unsigned)y[0], (unsigned)y[1]};
   };
 
   // ---- fragment read addresses.  A: row wm*64 + i*16 + (lane&15), chunk lane>>4;
@@ -359,15 +377,29 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     // four uses and is refilled with the next K-block's; partials pass through
     // a ring of PDEPTH partials so PDEPTH MFMAs are in flight while the VALU
     // promotes the oldest.  The staging of K-block kb+2 (decode + LDS stores)
-    // goes in after the fifth MFMA.
+    // is cut into four pieces spread over the MFMA sequence, so that no stretch
+    // of the iteration is conversions alone.
+    //
+    // Wave priority falls in steps over the iteration (3 at its start, 0 from
+    // the 30th step on).  A SIMD runs two waves of the tile; at equal priority
+    // the older one issues first, runs ahead, and then waits at the barrier
+    // while the other finishes alone.  Measured with per-wave cycle counters
+    // at 4096^3: the leading waves waited 706 cycles per K-block at the
+    // barrier, the others 106, in 2330-cycle K-blocks.  With the priority
+    // steps the wave that is behind in the iteration issues first, the two
+    // stay close, and the kernel took 139 us against 145.
     constexpr int PDEPTH = 6;
     v4f pr[PDEPTH];
     if constexpr (!COMPUTE) {
       store_stage(sf, ra, rb);
       load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
     }
+    if constexpr (COMPUTE) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int q = 0; q < (COMPUTE ? 32 + PDEPTH : 0); ++q) {
+      if (q == 10) __builtin_amdgcn_s_setprio(2);
+      if (q == 20) __builtin_amdgcn_s_setprio(1);
+      if (q == 30) __builtin_amdgcn_s_setprio(0);
       if (q >= PDEPTH) {
         const int u = q - PDEPTH;
         const int ui = u & 3, uj = u >> 2;
@@ -384,12 +416,19 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
         if (qi == 3) bfrag[qj] = read_b(sn, qj);  // last use of this B fragment
         if (qj == 7) af[qi] = read_a(sn, qi);     // last use of this A fragment
       }
-      if (q == 4) {
-        // Unconditional (clamped) staging: a branch here would keep the old and
-        // new register contents alive together.  Past the end the stage written
-        // is never read.
-        store_stage(sf, ra, rb);
-        load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
+      // Unconditional (clamped) staging: a branch here would keep the old and
+      // new register contents alive together.  Past the end the stage written
+      // is never read.  Each register is reloaded (K-block kb+4) as soon as
+      // both of its halves are staged, A before B as in the prologue.
+      if (q == 4) store_piece(sf, 0, ra, rb);
+      if (q == 10) {
+        store_piece(sf, 1, ra, rb);
+        load_a_only(kb + 4 < KB ? kb + 4 : KB - 1, ra);
+      }
+      if (q == 16) store_piece(sf, 2, ra, rb);
+      if (q == 22) {
+        store_piece(sf, 3, ra, rb);
+        load_b_only(kb + 4 < KB ? kb + 4 : KB - 1, rb);
       }
       // scheduling groups of three MFMAs: every promotion in a group reads a
       // partial formed at least one group earlier, so the compiler never has
