@@ -94,8 +94,16 @@ struct TileArgs {
 // block): the scale sa[row, kb] * sb[kb, cb] is one value per lane per
 // sub-tile.  Every kernel that takes token-group scales forms its partials
 // this way.
-template <bool BT, bool TG>
+//
+// LIGHT: a tile with at most 128 rows of the problem.  The staging, the LDS
+// layout and the scale window are the full tile's, but the eight waves cover
+// the first 128 rows only: two row bands of 64 and four column bands of 64
+// (a 64 x 64 wave tile).  With 65-128 rows every SIMD runs two busy waves;
+// with at most 64, one.  Each output element is formed by the same MFMAs and
+// promotions in the same order as in the full tile.
+template <bool BT, bool TG, bool LIGHT = false>
 __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem) {
+  static_assert(!(LIGHT && TG), "the light tile is used with 32x32 scales only");
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = wave_id_uniform();
@@ -103,8 +111,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // row band wm = w >> 1 gives every SIMD one wave in the tile's upper half
   // and one in its lower half: in a tile whose last rows lie past the
   // problem, the waves of bands with no rows skip their MFMAs and promotions
-  // and every SIMD keeps one busy wave.
-  const int wm = w >> 1, wn = w & 1;
+  // and every SIMD keeps one busy wave.  In a light tile, waves w and w + 4
+  // (one SIMD) take the two row bands of column band w & 3.
+  constexpr int JN = LIGHT ? 4 : 8;           // 16-column sub-tiles per wave
+  constexpr int WN_T = JN * 16;               // columns per wave
+  constexpr int NQ = 4 * JN;                  // MFMAs per wave and K-block
+  const int wm = LIGHT ? (w >> 2) : (w >> 1);
+  const int wn = LIGHT ? (w & 3) : (w & 1);
   const int64_t K = p.K, N = p.N;
   const int KB = (int)(K >> 5);
   const int NB = (int)(N >> 5);
@@ -186,20 +199,20 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   const int fr_lo = lane & 15, fr_kc = lane >> 4;
   const lds_u8* const rd_a = sA + a_lds_off(wm * 64 + fr_lo, fr_kc);
   // B (transposed reads): lane (g, r, c) = (lane>>4, (lane>>2)&3, lane&3) reads row
-  // k = 8g + 4h + r, 32-byte chunk J = wn*8 + j at position J ^ r, byte 8c.
-  // J ^ r = wn*8 + 4*(j>>2) + ((j&3) ^ r): four lane-dependent bases, the rest
+  // k = 8g + 4h + r, 32-byte chunk J = wn*JN + j at position J ^ r, byte 8c.
+  // J ^ r = wn*JN + 4*(j>>2) + ((j&3) ^ r): four lane-dependent bases, the rest
   // (h, j>>2, the stage) compile-time offsets.
   const int tr_g = lane >> 4, tr_r = (lane >> 2) & 3, tr_c = lane & 3;
   const lds_u8* rd_b[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj)
-    rd_b[jj] = sB + b_lds_off(8 * tr_g + tr_r, wn * 8 + jj) + tr_c * 8;
+    rd_b[jj] = sB + b_lds_off(8 * tr_g + tr_r, wn * JN + jj) + tr_c * 8;
   auto read_a = [&](int st, int i) __attribute__((always_inline)) -> v8bf {
     typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
     return *(lds_v8bf*)(rd_a + st * A_STAGE_BYTES + i * 1024);
   };
-  // B^T: weight row wn*128 + j*16 + (lane&15), chunk lane>>4, read like A
-  const lds_u8* const rd_bt = sB + a_lds_off(wn * 128 + fr_lo, fr_kc);
+  // B^T: weight row wn*WN_T + j*16 + (lane&15), chunk lane>>4, read like A
+  const lds_u8* const rd_bt = sB + a_lds_off(wn * WN_T + fr_lo, fr_kc);
   auto read_b = [&](int st, int j) __attribute__((always_inline)) -> v8bf {
     if constexpr (BT) {
       typedef __attribute__((address_space(3))) const v8bf lds_v8bf;
@@ -241,16 +254,29 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     for (int i = 0; i < SCW / 8; ++i)
       dst[(w_k0 + 8 * i) * 64 + w_rb * 8 + w_cb] = win * SCW + w_k0 + 8 * i < KB ? va[i] * vb[i] : 0.0f;
   };
-  // this wave's blocks: rows wm*64.. (row-blocks 2wm, 2wm+1), cols wn*128.. (col-blocks 4wn..4wn+3)
+  // this wave's blocks: rows wm*64.. (row-blocks 2wm, 2wm+1), cols wn*WN_T..
+  // (col-blocks CBW*wn .. CBW*wn + CBW-1)
   typedef float v4f_t __attribute__((ext_vector_type(4)));
-  auto read_scales = [&](int kb, float (&sc)[2][4]) __attribute__((always_inline)) {
-    const float* w0 = sc_lds + ((kb / SCW) & 1) * (SCW * 64) + (kb % SCW) * 64 + (2 * wm) * 8 + 4 * wn;
-    const v4f_t r0 = *reinterpret_cast<const v4f_t*>(w0);
-    const v4f_t r1 = *reinterpret_cast<const v4f_t*>(w0 + 8);
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  constexpr int CBW = JN / 2;
+  auto read_scales = [&](int kb, float (&sc)[2][CBW]) __attribute__((always_inline)) {
+    const float* w0 = sc_lds + ((kb / SCW) & 1) * (SCW * 64) + (kb % SCW) * 64 + (2 * wm) * 8 + CBW * wn;
+    if constexpr (CBW == 4) {
+      const v4f_t r0 = *reinterpret_cast<const v4f_t*>(w0);
+      const v4f_t r1 = *reinterpret_cast<const v4f_t*>(w0 + 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[0][j] = r0[j];
-      sc[1][j] = r1[j];
+      for (int j = 0; j < 4; ++j) {
+        sc[0][j] = r0[j];
+        sc[1][j] = r1[j];
+      }
+    } else {
+      const v2f_t r0 = *reinterpret_cast<const v2f_t*>(w0);
+      const v2f_t r1 = *reinterpret_cast<const v2f_t*>(w0 + 8);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        sc[0][j] = r0[j];
+        sc[1][j] = r1[j];
+      }
     }
   };
 
@@ -299,11 +325,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     for (int j = 0; j < 4; ++j) sbs[j] = uniform_f32(sb4[j]);
   };
 
-  v4f acc[4][8];
+  v4f acc[4][JN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   // ---- prologue: K-blocks 0 and 1 staged in LDS, K-blocks 2 and 3 in the two
   // register sets, K-block 0's fragments in registers
@@ -333,12 +359,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  v8bf af[4], bfrag[8];
+  v8bf af[4], bfrag[JN];
   if (KB > 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[i] = read_a(0, i);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bfrag[j] = read_b(0, j);
+    for (int j = 0; j < JN; ++j) bfrag[j] = read_b(0, j);
   }
 
   // Ring of three bf16 stages: in the iteration for K-block kb (stage kb%3 is
@@ -350,7 +376,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // the scale products of the current K-block; those of the next are read
   // right after the last promotion, into the same registers, so the barrier
   // hides the LDS latency
-  float s_cur[2][4];
+  float s_cur[2][CBW];
   v4f_t sa4 = {0.0f, 0.0f, 0.0f, 0.0f}, s4 = {0.0f, 0.0f, 0.0f, 0.0f};
   float sbs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (KB > 0) {
@@ -381,7 +407,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     // of the iteration is conversions alone.
     //
     // Wave priority falls in steps over the iteration (3 at its start, 0 from
-    // the 30th step on).  A SIMD runs two waves of the tile; at equal priority
+    // the 30th of 38 steps on; proportionally in a light tile).  A SIMD runs two waves of the tile; at equal priority
     // the older one issues first, runs ahead, and then waits at the barrier
     // while the other finishes alone.  Measured with per-wave cycle counters
     // at 4096^3: the leading waves waited 706 cycles per K-block at the
@@ -394,12 +420,14 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       store_stage(sf, ra, rb);
       load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
     }
+    constexpr int QP2 = NQ * 10 / 32, QP1 = NQ * 20 / 32, QP0 = NQ * 30 / 32;  // priority steps
+    constexpr int QS0 = NQ * 4 / 32, QS1 = NQ * 10 / 32, QS2 = NQ * 16 / 32, QS3 = NQ * 22 / 32;  // staging
     if constexpr (COMPUTE) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-    for (int q = 0; q < (COMPUTE ? 32 + PDEPTH : 0); ++q) {
-      if (q == 10) __builtin_amdgcn_s_setprio(2);
-      if (q == 20) __builtin_amdgcn_s_setprio(1);
-      if (q == 30) __builtin_amdgcn_s_setprio(0);
+    for (int q = 0; q < (COMPUTE ? NQ + PDEPTH : 0); ++q) {
+      if (q == QP2) __builtin_amdgcn_s_setprio(2);
+      if (q == QP1) __builtin_amdgcn_s_setprio(1);
+      if (q == QP0) __builtin_amdgcn_s_setprio(0);
       if (q >= PDEPTH) {
         const int u = q - PDEPTH;
         const int ui = u & 3, uj = u >> 2;
@@ -410,23 +438,23 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
           promote(acc[ui][uj], pr[u % PDEPTH], s_cur[ui >> 1][uj >> 1]);
         }
       }
-      if (q < 32) {
+      if (q < NQ) {
         const int qi = q & 3, qj = q >> 2;
         pr[q % PDEPTH] = TG ? mfma_partial(bfrag[qj], af[qi]) : mfma_partial(af[qi], bfrag[qj]);
-        if (qi == 3) bfrag[qj] = read_b(sn, qj);  // last use of this B fragment
-        if (qj == 7) af[qi] = read_a(sn, qi);     // last use of this A fragment
+        if (qi == 3) bfrag[qj] = read_b(sn, qj);   // last use of this B fragment
+        if (qj == JN - 1) af[qi] = read_a(sn, qi);  // last use of this A fragment
       }
       // Unconditional (clamped) staging: a branch here would keep the old and
       // new register contents alive together.  Past the end the stage written
       // is never read.  Each register is reloaded (K-block kb+4) as soon as
       // both of its halves are staged, A before B as in the prologue.
-      if (q == 4) store_piece(sf, 0, ra, rb);
-      if (q == 10) {
+      if (q == QS0) store_piece(sf, 0, ra, rb);
+      if (q == QS1) {
         store_piece(sf, 1, ra, rb);
         load_a_only(kb + 4 < KB ? kb + 4 : KB - 1, ra);
       }
-      if (q == 16) store_piece(sf, 2, ra, rb);
-      if (q == 22) {
+      if (q == QS2) store_piece(sf, 2, ra, rb);
+      if (q == QS3) {
         store_piece(sf, 3, ra, rb);
         load_b_only(kb + 4 < KB ? kb + 4 : KB - 1, rb);
       }
@@ -456,7 +484,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   // finite (a partial of finite codes).  A zero acc may change sign there;
   // the epilogue stores every exact zero as +0 (bf16_out), so the stored bits
   // equal those of a kernel that stops at the last K-block.
-  if (p.row0 + wm * 64 < p.row_end) {
+  if (p.row0 + wm * 64 < p.row_end) {   // this wave's row band holds rows of the problem
     for (int kb = 0; kb < KB; kb += 2) {
       iteration(kb, ra, rb, std::true_type{});
       iteration(kb + 1, ra2, rb2, std::true_type{});
@@ -468,29 +496,31 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     }
   }
 
-  // ---- epilogue: bf16, through LDS (per-wave 32x128 region, two passes) for
+  // ---- epilogue: bf16, through LDS (per-wave 32 x WN_T region, two passes) for
   // 16-byte coalesced global stores
-  unsigned char* ep = smem + w * (32 * 128 * 2);
+  constexpr int EP_ROW = WN_T * 2;        // bytes per row of the region
+  constexpr int EP_LPR = WN_T / 8;        // lanes per row in the store pass
+  unsigned char* ep = smem + w * (32 * EP_ROW);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = pass * 2 + ii;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < JN; ++j) {
         if constexpr (TG) {
           // lane holds row ii*16 + (lane&15), columns j*16 + 4*(lane>>4) + 0..3
           const int lr = ii * 16 + (lane & 15);
           const int lc = j * 16 + 4 * (lane >> 4);
           const uint32_t lo = bf16_out(acc[i][j][0]) | (bf16_out(acc[i][j][1]) << 16);
           const uint32_t hi = bf16_out(acc[i][j][2]) | (bf16_out(acc[i][j][3]) << 16);
-          *reinterpret_cast<uint2*>(ep + lr * 256 + lc * 2) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(ep + lr * EP_ROW + lc * 2) = make_uint2(lo, hi);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int lr = ii * 16 + 4 * (lane >> 4) + r;
             const int lc = j * 16 + (lane & 15);
-            *reinterpret_cast<uint16_t*>(ep + lr * 256 + lc * 2) = (uint16_t)bf16_out(acc[i][j][r]);
+            *reinterpret_cast<uint16_t*>(ep + lr * EP_ROW + lc * 2) = (uint16_t)bf16_out(acc[i][j][r]);
           }
         }
       }
@@ -498,12 +528,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int lr = it * 4 + (lane >> 4);
-      const int lc = (lane & 15) * 8;
-      uint4 v = *reinterpret_cast<const uint4*>(ep + lr * 256 + lc * 2);
+    for (int it = 0; it < 32 * EP_LPR / 64; ++it) {
+      const int lr = it * (64 / EP_LPR) + lane / EP_LPR;
+      const int lc = (lane % EP_LPR) * 8;
+      uint4 v = *reinterpret_cast<const uint4*>(ep + lr * EP_ROW + lc * 2);
       const int64_t grow = p.row0 + wm * 64 + pass * 32 + lr;
-      const int64_t gcol = p.col0 + wn * 128 + lc;
+      const int64_t gcol = p.col0 + wn * WN_T + lc;
       if (grow < p.row_end && gcol < N) *reinterpret_cast<uint4*>(p.c + grow * N + gcol) = v;
     }
     __builtin_amdgcn_wave_barrier();
@@ -555,7 +585,13 @@ __global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __re
   p.row_end = M;
   p.col0 = tn * TBN;
   p.sa_rows = (M + 31) >> 5;
-  tile_body<BT, TG>(p, smem);
+  if constexpr (!TG) {
+    // a last M-tile of at most 128 rows runs as a light tile
+    if (M - p.row0 <= 128) tile_body<BT, TG, true>(p, smem);
+    else tile_body<BT, TG>(p, smem);
+  } else {
+    tile_body<BT, TG>(p, smem);
+  }
 }
 
 // Grouped GEMM (DeepGEMM write-up, sections 4.1-4.3): group g owns rows
@@ -673,7 +709,8 @@ __global__ void __launch_bounds__(TTHREADS) gemm_grouped_kernel(const uint8_t* _
     p.row_end = end;
     p.col0 = tn * TBN;
     p.sa_rows = M_total >> 5;
-    tile_body<BT, false>(p, smem);
+    if (cls == 0) tile_body<BT, false>(p, smem);
+    else tile_body<BT, false, true>(p, smem);
   }
 }
 

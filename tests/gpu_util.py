@@ -60,5 +60,11 @@ def gpu_grouped(qa, sa, qb, sb, offsets, c_init=None):
     return bits_np(c)
 
 
+def gpu_grouped_nt(qa, sa, qbt, sbt, offsets):
+    c = fp8bs.grouped_gemm_nt(u8_dev(qa), f32_dev(sa), u8_dev(qbt), f32_dev(sbt), i32_dev(offsets))
+    torch.cuda.synchronize()
+    return bits_np(c)
+
+
 def bits_to_f64(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

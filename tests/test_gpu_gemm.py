@@ -8,7 +8,7 @@ import oracle
 import fp8_block_scaled_03_amd as fp8bs
 from fp8_block_scaled_03_amd import workloads as W
 
-from gpu_util import bits_np, bits_to_f64, f32_dev, gpu_gemm, gpu_grouped, say, u8_dev
+from gpu_util import bits_np, bits_to_f64, f32_dev, gpu_gemm, gpu_grouped, gpu_grouped_nt, say, u8_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -157,7 +157,8 @@ def test_zero_results_are_plus_zero_in_every_kernel():
 
 def test_rows_independent_of_batch():
     """Row i of C is bitwise the same computed alone (M=1, small-M kernel),
-    inside M=64 (small-M kernel) and inside M=320 (tile kernel)."""
+    inside M=64 (small-M kernel), inside M=100 (one light tile), M=200 and
+    M=320 (tile kernel; the last 64 rows of M=320 form a light tile)."""
     qa, sa = _quantized(25, 320, 256)
     qb, sb = _quantized(26, 256, 96, std=0.02)
     say("invariance full M=320")
@@ -165,6 +166,9 @@ def test_rows_independent_of_batch():
     say("invariance M=64")
     part = gpu_gemm(qa[:64], sa[:2], qb, sb)
     assert np.array_equal(part, full[:64])
+    say("invariance M=100 (a light tile) and M=200 (a full one)")
+    assert np.array_equal(gpu_gemm(qa[:100], sa[:4], qb, sb), full[:100])
+    assert np.array_equal(gpu_gemm(qa[:200], sa[:7], qb, sb), full[:200])
     for i in (0, 5, 31, 32, 63, 64, 100, 255, 319):
         say(f"invariance row {i}")
         one = gpu_gemm(qa[i:i + 1], sa[i // 32:i // 32 + 1], qb, sb)
@@ -266,6 +270,35 @@ def test_grouped_many_groups_heavy_and_light_tiles():
         r0, r1 = int(off[gi]), int(off[gi + 1])
         if r1 > r0:
             say(f"grouped many groups: group {gi} as a single GEMM")
+            assert np.array_equal(c[r0:r1], gpu_gemm(qa[r0:r1], sa[r0 // 32:r1 // 32], qb[gi], sb[gi])), gi
+
+
+@pytest.mark.parametrize("K", [352, 64])   # eleven K-blocks (odd), two
+def test_grouped_light_tiles_every_column_band(K):
+    """Group tails of at most 128 rows run as light tiles (eight 64 x 64 wave
+    tiles over 128 rows x 256 columns): tails of 32, 64, 96 and 128 rows, and
+    groups with full tiles before them, at N = 544 (two full column tiles and
+    a 32-column rest).  Each group equals a single GEMM of its rows bitwise,
+    in both weight layouts, and the whole output is within the bound."""
+    G, N = 7, 544
+    rows = np.array([32, 64, 96, 128, 288, 416, 0])
+    off = W.offsets_from_rows(rows)
+    M = int(off[-1])
+    qa, sa = _quantized(90, M, K)
+    qb = np.stack([_quantized(91 + i, K, N, std=0.02)[0] for i in range(G)])
+    sb = np.stack([_quantized(91 + i, K, N, std=0.02)[1] for i in range(G)])
+    say(f"grouped light tiles K={K}")
+    c = gpu_grouped(qa, sa, qb, sb, off)
+    ref, absref = oracle.grouped_gemm_ref(qa, sa, qb, sb, off)
+    _assert_tol(c, ref, absref, "grouped light tiles")
+    qbt = np.ascontiguousarray(qb.transpose(0, 2, 1))
+    sbt = np.ascontiguousarray(sb.transpose(0, 2, 1))
+    say("grouped light tiles, K-major weight")
+    assert np.array_equal(c, gpu_grouped_nt(qa, sa, qbt, sbt, off))
+    for gi in range(G):
+        r0, r1 = int(off[gi]), int(off[gi + 1])
+        if r1 > r0:
+            say(f"grouped light tiles: group {gi} ({r1 - r0} rows) as a single GEMM")
             assert np.array_equal(c[r0:r1], gpu_gemm(qa[r0:r1], sa[r0 // 32:r1 // 32], qb[gi], sb[gi])), gi
 
 

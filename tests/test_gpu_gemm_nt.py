@@ -11,7 +11,8 @@ import fp8_block_scaled_03_amd as fp8bs
 from fp8_block_scaled_03_amd import workloads as W
 
 import fullsize_util as FU
-from gpu_util import DEV, bf16_dev, bits_np, bits_to_f64, f32_dev, gpu_gemm, gpu_grouped, i32_dev, say, u8_dev
+from gpu_util import (DEV, bf16_dev, bits_np, bits_to_f64, f32_dev, gpu_gemm, gpu_grouped, gpu_grouped_nt, i32_dev, say,
+                      u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +23,6 @@ def _quantized(seed, rows, cols, std=1.0):
 
 def gpu_gemm_nt(qa, sa, qbt, sbt):
     c = fp8bs.gemm_nt(u8_dev(qa), f32_dev(sa), u8_dev(qbt), f32_dev(sbt))
-    torch.cuda.synchronize()
-    return bits_np(c)
-
-
-def gpu_grouped_nt(qa, sa, qbt, sbt, offsets):
-    c = fp8bs.grouped_gemm_nt(u8_dev(qa), f32_dev(sa), u8_dev(qbt), f32_dev(sbt), i32_dev(offsets))
     torch.cuda.synchronize()
     return bits_np(c)
 
