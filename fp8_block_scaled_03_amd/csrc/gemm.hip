@@ -44,18 +44,19 @@ constexpr int TBM = 256, TBN = 256, TTHREADS = 512;
 constexpr int A_STAGE_BYTES = TBM * 32 * 2;  // 16 KB bf16
 constexpr int B_STAGE_BYTES = 32 * TBN * 2 + 512;  // 16 KB bf16 + row-group shifts
 constexpr int STAGE_BYTES = A_STAGE_BYTES + B_STAGE_BYTES;
-constexpr int TILE_STAGES = 3;
+constexpr int TILE_STAGES = 4;
 // Scale products s = sa * sb are formed once per workgroup in windows of SCW
 // K-blocks (double-buffered in LDS): per K-block 8 row-blocks x 8 column-blocks.
-constexpr int SCW = 64;
-constexpr int SC_WINDOW_BYTES = SCW * 8 * 8 * 4;  // 16 KB
+constexpr int SCW = 32;
+constexpr int SC_WINDOW_BYTES = SCW * 8 * 8 * 4;  // 8 KB
 // Per-token-group activation scales: the window holds raw sa of the tile's 256
 // rows and raw sb of its 8 column blocks for SCWT K-blocks.
-constexpr int SCWT = 16;
+constexpr int SCWT = 8;
 constexpr int TG_WINDOW_FLOATS = SCWT * (256 + 8);
-constexpr int TG_WINDOW_BYTES = TG_WINDOW_FLOATS * 4;  // 16.5 KB
+constexpr int TG_WINDOW_BYTES = TG_WINDOW_FLOATS * 4;  // 8.25 KB
 constexpr int TILE_SC_BYTES = 2 * (SC_WINDOW_BYTES > TG_WINDOW_BYTES ? SC_WINDOW_BYTES : TG_WINDOW_BYTES);
-constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + TILE_SC_BYTES;  // 131 KB
+constexpr int TILE_LDS_BYTES = TILE_STAGES * STAGE_BYTES + TILE_SC_BYTES;  // 146.5 KB
+static_assert(TILE_LDS_BYTES <= 160 * 1024, "LDS budget");
 
 // A tile in LDS: [256 rows][4 chunks of 8 bf16]; chunk c of row r lives at
 // position c ^ ((r >> 1) & 3).
@@ -331,7 +332,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
 #pragma unroll
     for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // ---- prologue: K-blocks 0 and 1 staged in LDS, K-blocks 2 and 3 in the two
+  // ---- prologue: K-blocks 0-2 staged in LDS, K-blocks 3 and 4 in the two
   // register sets, K-block 0's fragments in registers
   // K = 0: no operand or scale is touched (the caller may pass null pointers);
   // the accumulators stay zero.
@@ -344,18 +345,19 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     }
   }
   uint4 ra = make_uint4(0, 0, 0, 0), rb = make_uint4(0, 0, 0, 0);
+  // stages 0-2 hold K-blocks 0-2, clamped to the last one: the empty K-blocks
+  // that pad KB to a multiple of four multiply finite codes
   if (KB > 0) { load_stage(0, ra, rb); store_stage(0, ra, rb); }
-  // stage 1 always holds finite codes (K-block 0 again when K has one block):
-  // an empty K-block after an odd last one multiplies whatever stage it reads
-  if (KB > 0) { load_stage(KB > 1 ? 1 : 0, ra, rb); store_stage(1, ra, rb); }
+  if (KB > 0) { load_stage(KB > 1 ? 1 : KB - 1, ra, rb); store_stage(1, ra, rb); }
+  if (KB > 0) { load_stage(KB > 2 ? 2 : KB - 1, ra, rb); store_stage(2, ra, rb); }
   // The two register sets are loaded in the order the loop reloads them (A then
   // B of the first set, then the second): the loop entry then matches the
   // steady state, and the compiler can count the loads in flight exactly.
   uint4 ra2 = make_uint4(0, 0, 0, 0), rb2 = make_uint4(0, 0, 0, 0);
   if (KB > 0) {
-    load_stage(KB > 2 ? 2 : KB - 1, ra, rb);
+    load_stage(KB > 3 ? 3 : KB - 1, ra, rb);
     __builtin_amdgcn_sched_barrier(0);
-    load_stage(KB > 3 ? 3 : KB - 1, ra2, rb2);
+    load_stage(KB > 4 ? 4 : KB - 1, ra2, rb2);
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
@@ -367,12 +369,16 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     for (int j = 0; j < JN; ++j) bfrag[j] = read_b(0, j);
   }
 
-  // Ring of three bf16 stages: in the iteration for K-block kb (stage kb%3 is
-  // already in registers), stage (kb+1)%3 (written one iteration earlier) is
-  // read for the next iteration while this one computes, and stage (kb+2)%3
-  // receives the K-block held in registers.  One barrier per iteration orders
-  // the three.
-  int sn = 1, sf = 2;  // stages (kb+1)%3 and (kb+2)%3, wave-uniform
+  // Ring of four bf16 stages: in the iteration for K-block kb (stage kb%4 is
+  // already in registers), stage (kb+1)%4 is read for the next iteration
+  // while this one computes, and stage (kb+3)%4 receives the K-block held in
+  // registers.  A barrier after every second iteration orders them: a stage
+  // written in iteration kb is read in iteration kb+2 at the earliest, and the
+  // stage it overwrites was last read in iteration kb-2, both across a
+  // barrier.  The loop runs four iterations per trip, so every stage offset
+  // is a constant (measured 137 against 139 us at 4096^3 with three stages
+  // and one barrier per K-block).
+
   // the scale products of the current K-block; those of the next are read
   // right after the last promotion, into the same registers, so the barrier
   // hides the LDS latency
@@ -384,13 +390,15 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     else read_scales(0, s_cur);
   }
   // Two register sets alternate between iterations: the global loads of a
-  // K-block are issued two iterations before its staging, so their latency
-  // hides behind two iterations of MFMAs.
+  // K-block (kb+5 in iteration kb) are issued two iterations before its
+  // staging, so their latency hides behind two iterations of MFMAs.
   // `compute_tag` (std::true_type / std::false_type): false for a wave whose
   // row band holds no rows of the problem; it then only stages, refills the
   // scale windows and meets the barriers.
-  auto iteration = [&](int kb, uint4& ra, uint4& rb, auto compute_tag) __attribute__((always_inline)) {
+  auto iteration = [&](int kb, uint4& ra, uint4& rb, auto compute_tag, auto phase_tag) __attribute__((always_inline)) {
     constexpr bool COMPUTE = decltype(compute_tag)::value;
+    constexpr int J = decltype(phase_tag)::value;        // kb % 4
+    constexpr int sn = (J + 1) & 3, sf = (J + 3) & 3;    // stages of K-blocks kb+1 and kb+3
     // next window of scales: written now, first read SCW (SCWT) iterations later
     const bool tg_refill = TG && kb % SCWT == 0 && kb + SCWT < KB;
     if constexpr (TG) {
@@ -418,7 +426,7 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     v4f pr[PDEPTH];
     if constexpr (!COMPUTE) {
       store_stage(sf, ra, rb);
-      load_stage(kb + 4 < KB ? kb + 4 : KB - 1, ra, rb);
+      load_stage(kb + 5 < KB ? kb + 5 : KB - 1, ra, rb);
     }
     constexpr int QP2 = NQ * 10 / 32, QP1 = NQ * 20 / 32, QP0 = NQ * 30 / 32;  // priority steps
     constexpr int QS0 = NQ * 4 / 32, QS1 = NQ * 10 / 32, QS2 = NQ * 16 / 32, QS3 = NQ * 22 / 32;  // staging
@@ -451,12 +459,12 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       if (q == QS0) store_piece(sf, 0, ra, rb);
       if (q == QS1) {
         store_piece(sf, 1, ra, rb);
-        load_a_only(kb + 4 < KB ? kb + 4 : KB - 1, ra);
+        load_a_only(kb + 5 < KB ? kb + 5 : KB - 1, ra);
       }
       if (q == QS2) store_piece(sf, 2, ra, rb);
       if (q == QS3) {
         store_piece(sf, 3, ra, rb);
-        load_b_only(kb + 4 < KB ? kb + 4 : KB - 1, rb);
+        load_b_only(kb + 5 < KB ? kb + 5 : KB - 1, rb);
       }
       // scheduling groups of three MFMAs: every promotion in a group reads a
       // partial formed at least one group earlier, so the compiler never has
@@ -467,32 +475,39 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
       if constexpr (TG) read_tg_scales(kb + 1, sa4, sbs);
       else read_scales(kb + 1, s_cur);
     }
-    // the window's direct loads have landed before the barrier publishes them
-    // (every iteration: a wait under a branch here costs the loop its
-    // registers).  Only this iteration's two operand loads were issued after
-    // them, and they may stay in flight.
-    if constexpr (TG) wait_vmcnt<2>();
-    __syncthreads();
-    sn = sn == 2 ? 0 : sn + 1;
-    sf = sf == 2 ? 0 : sf + 1;
+    // the window's direct loads (issued at the start of an even iteration)
+    // have landed before the barrier that publishes them: only the operand
+    // loads of that iteration and the next (four) were issued after them.
+    if constexpr (J & 1) {
+      if constexpr (TG) wait_vmcnt<4>();
+      __syncthreads();
+    }
   };
-  // Both iterations of the pair are unconditional: a conditional second one
-  // would give the loop's back edge two different orders of loads in flight,
-  // and the compiler would then wait for all of them before staging.  An odd
-  // last K-block is paired with an empty one (kb = KB) whose scale products
+  // All four iterations of a trip are unconditional: a conditional one would
+  // give the loop's back edge different orders of loads in flight, and the
+  // compiler would then wait for all of them before staging.  KB is padded
+  // to a multiple of four with empty K-blocks (kb >= KB) whose scale products
   // are zero: fma(P, 0, acc) returns acc for every nonzero acc, since P is
   // finite (a partial of finite codes).  A zero acc may change sign there;
   // the epilogue stores every exact zero as +0 (bf16_out), so the stored bits
   // equal those of a kernel that stops at the last K-block.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
   if (p.row0 + wm * 64 < p.row_end) {   // this wave's row band holds rows of the problem
-    for (int kb = 0; kb < KB; kb += 2) {
-      iteration(kb, ra, rb, std::true_type{});
-      iteration(kb + 1, ra2, rb2, std::true_type{});
+    for (int kb = 0; kb < KB; kb += 4) {
+      iteration(kb, ra, rb, std::true_type{}, P0{});
+      iteration(kb + 1, ra2, rb2, std::true_type{}, P1{});
+      iteration(kb + 2, ra, rb, std::true_type{}, P2{});
+      iteration(kb + 3, ra2, rb2, std::true_type{}, P3{});
     }
   } else {
-    for (int kb = 0; kb < KB; kb += 2) {
-      iteration(kb, ra, rb, std::false_type{});
-      iteration(kb + 1, ra2, rb2, std::false_type{});
+    for (int kb = 0; kb < KB; kb += 4) {
+      iteration(kb, ra, rb, std::false_type{}, P0{});
+      iteration(kb + 1, ra2, rb2, std::false_type{}, P1{});
+      iteration(kb + 2, ra, rb, std::false_type{}, P2{});
+      iteration(kb + 3, ra2, rb2, std::false_type{}, P3{});
     }
   }
 
