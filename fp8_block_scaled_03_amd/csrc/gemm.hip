@@ -13,15 +13,17 @@
 //    a 256x256 C tile; eight waves in a 4(M) x 2(N) grid own 64x128 each
 //    (4 x 8 MFMA sub-tiles of 16x16).  Per 32-deep K-block the workgroup
 //    loads 8 KB of A and 8 KB of B (16 bytes per thread each, coalesced, two
-//    K-blocks ahead in two register sets), decodes E4M3 -> bf16 once, and
-//    stores the bf16 tiles into a three-stage LDS ring with an XOR swizzle so
-//    that the fragment reads are free of bank conflicts (DeepGEMM write-up,
-//    section 3.1, makes the same point for shared memory; section 3.3 for
-//    overlapping the next tile's loads with compute).  A fragments are read
-//    K-contiguous with ds_read_b128; B is N-contiguous in memory, so its
-//    fragments come from the LDS transpose read ds_read_b64_tr_b16 (a K-major
-//    weight is staged like A instead).  Waves whose 64-row band lies wholly
-//    past the problem's rows only stage and meet the barriers.
+//    iterations ahead in two register sets), decodes E4M3 -> bf16 once, and
+//    stores the bf16 tiles into a four-stage LDS ring (one barrier per two
+//    K-blocks) with an XOR swizzle so that the fragment reads are free of
+//    bank conflicts (DeepGEMM write-up, section 3.1, makes the same point for
+//    shared memory; section 3.3 for overlapping the next tile's loads with
+//    compute).  A fragments are read K-contiguous with ds_read_b128; B is
+//    N-contiguous in memory, so its fragments come from the LDS transpose read
+//    ds_read_b64_tr_b16 (a K-major weight is staged like A instead).  Waves
+//    whose 64-row band lies wholly past the problem's rows only stage and meet
+//    the barriers; a tile with at most 128 rows runs the light body (eight
+//    64 x 64 wave tiles over 128 x 256).
 //  * small-M kernels (M <= 64, decode): a workgroup owns a slice of 32, 64 or
 //    128 columns of C for all rows and all of K and streams its slice of the
 //    weight once, eight K-blocks per round, with direct global->LDS loads into
