@@ -557,23 +557,6 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
   }
 }
 
-// Tile order: consecutive workgroup ids are dealt round-robin to the 8 XCDs, so
-// ids are first re-dealt so that each XCD sees a contiguous run of tiles; the
-// run is walked in groups of 4 M-tiles so that neighbours share A rows and B
-// columns in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int64_t id, int64_t n_tiles, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  const int64_t per_xcd = (n_tiles + 7) / 8;
-  const int64_t lin = (id & 7) * per_xcd + (id >> 3);  // callers remap only when n_tiles % 8 == 0
-  const int64_t GM = 4;
-  const int64_t group = lin / (GM * tiles_n);
-  const int64_t first_m = group * GM;
-  const int64_t tiles_m_total = (n_tiles / tiles_n);
-  const int64_t gm = (tiles_m_total - first_m) < GM ? (tiles_m_total - first_m) : GM;
-  const int64_t r = lin - group * GM * tiles_n;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
-
 template <bool BT, bool TG>
 __global__ void __launch_bounds__(TTHREADS) gemm_tile_kernel(const uint8_t* __restrict__ a,
                                                              const float* __restrict__ sa,

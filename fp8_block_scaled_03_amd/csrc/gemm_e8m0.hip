@@ -17,12 +17,14 @@
 // comes from lane 16*kb + r.  The first operand's rows are C's columns here
 // (the weight), so a lane's four results are four columns of one row.
 //
-// Tile: 128 x 128 per 256-thread workgroup; four waves of 64 x 64 (4 x 4
-// sub-tiles).  A and Bt are streamed as E4M3 bytes with direct global->LDS
-// loads into a ring of 128-deep K steps (two or three slots); row r of a stage holds its
-// 128 bytes with 16-byte piece p at position p ^ (r & 7).  Each stage also
-// carries the step's scale bytes (four K-blocks for the tile's four A
-// row-blocks and four Bt row-blocks).
+// Tiles: 256 x 256 per 512-thread workgroup (eight waves of 128 x 64) when
+// the grid fills the chip, else 128 x 128 per 256-thread workgroup (four
+// waves of 64 x 64).  A and Bt are streamed as E4M3 bytes with direct
+// global->LDS loads into a ring of 128-deep K steps (two slots, or three for
+// a small grid of 128 x 128 tiles); row r of a stage holds its 128 bytes with
+// 16-byte piece p at position p ^ (r & 7).  Each stage also carries the
+// step's scale bytes (four K-blocks for each of the tile's A and Bt
+// row-blocks).
 #include "common.hpp"
 
 namespace fp8bs {
@@ -38,6 +40,8 @@ constexpr int E_STAGE = E_SC_OFF + 4 * 256;       // one 256-byte record per wav
 // few workgroups of a decode-sized launch).  The per-element instruction
 // sequence is the same at either depth, so results do not change with M.
 constexpr int E_MANY_TILES = 512;
+// 256 x 256 tiles when they fill the chip at least once
+constexpr int64_t E_BIG_TILES = 256;
 
 template <int ESTAGES>
 __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* __restrict__ a,
@@ -143,6 +147,132 @@ __global__ void __launch_bounds__(ETHREADS) gemm_e8m0_nt_kernel(const uint8_t* _
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t row = row0 + wm * 64 + 16 * i + lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = col0 + wn * 64 + 16 * j + 4 * g;
+      if (row < M && col < N) {
+        const uint32_t w0 = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+        const uint32_t w1 = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(c + row * N + col) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+// ---- large grids: a 256 x 256 tile per 512-thread workgroup; eight waves of
+// 128 x 64 (8 x 4 sub-tiles), two row bands by four column bands.  Per
+// 128-deep step a wave reads 128 + 64 rows of fragments from LDS for 32
+// MFMAs, against 64 + 64 rows for 16 in the 128 x 128 tile, and the
+// workgroup stages 64 KB for 16.8 MFLOP against 32 KB for 4.2: a third less
+// LDS traffic per flop.  The per-element MFMA sequence (operands, scale bytes,
+// 128-deep steps in ascending K) is the 128 x 128 tile's, so the results are
+// bitwise the same.  Measured with flushed caches: 4096^3 84-88 -> 69-72 us,
+// 8192 x 28672 x 8192 2.12 -> 1.61 ms, and 1.54 ms with the XCD-aware order.
+constexpr int EB2M = 256, EB2N = 256, E2THREADS = 512;
+constexpr int E2_OPND_BYTES = EB2M * EBK;         // 32 KB per operand and stage
+constexpr int E2_SC_OFF = 2 * E2_OPND_BYTES;
+constexpr int E2_STAGE = E2_SC_OFF + 8 * 256;     // one 256-byte scale record per wave
+constexpr int E2_STAGES = 2;
+
+__global__ void __launch_bounds__(E2THREADS) gemm_e8m0_nt_big_kernel(const uint8_t* __restrict__ a,
+                                                                     const uint8_t* __restrict__ ea,
+                                                                     const uint8_t* __restrict__ bt,
+                                                                     const uint8_t* __restrict__ ebt,
+                                                                     uint16_t* __restrict__ c, int64_t M, int64_t N,
+                                                                     int64_t K, int64_t tiles_n, int remap) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const int wm = w & 1, wn = w >> 1;
+  int64_t tm, tn;
+  if (remap) {
+    tile_coords(blockIdx.x, gridDim.x, tiles_n, tm, tn);
+  } else {
+    tm = blockIdx.x / tiles_n;
+    tn = blockIdx.x % tiles_n;
+  }
+  const int64_t row0 = tm * EB2M, col0 = tn * EB2N;
+  const int KS = (int)(K / EBK);
+  const int64_t KB = K >> 5;
+
+  // ---- direct loads: wave w fills 1 KB pieces 4w..4w+3 of each operand
+  // (rows 8p..8p+7), as in the 128 x 128 kernel
+  const uint8_t* a_src[4];
+  const uint8_t* b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (w * 4 + i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    int64_t ar = row0 + r, br = col0 + r;
+    ar = ar < M ? ar : M - 1;
+    br = br < N ? br : N - 1;
+    a_src[i] = a + ar * K + chunk * 16;
+    b_src[i] = bt + br * K + chunk * 16;
+  }
+  // scale record: lanes 0-7 the tile's eight A row-blocks, lanes 8-15 its
+  // eight Bt row-blocks (clamped); 4 bytes each = the step's four K-blocks;
+  // lanes 16-63 repeat lane 15's entry
+  const int64_t nrb_a = (M + 31) >> 5, nrb_b = N >> 5;
+  const int sl = lane < 16 ? lane : 15;
+  const int64_t srb = sl < 8 ? (row0 >> 5) + sl : (col0 >> 5) + (sl - 8);
+  const uint8_t* sc_src = sl < 8 ? ea + (srb < nrb_a ? srb : nrb_a - 1) * KB
+                                 : ebt + (srb < nrb_b ? srb : nrb_b - 1) * KB;
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  const uint32_t ring = (uint32_t)(uintptr_t)((lds_u8*)smem);
+
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const uint32_t slot = ring + (step % E2_STAGES) * E2_STAGE;
+    const int ks = step < KS ? step : KS - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(a_src[i] + (int64_t)ks * EBK, slot + (w * 4 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(b_src[i] + (int64_t)ks * EBK, slot + E2_OPND_BYTES + (w * 4 + i) * 1024);
+    dma4(sc_src + (int64_t)ks * 4, slot + E2_SC_OFF + w * 256);
+  };
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int g = lane >> 4, lo = lane & 15;
+  auto frag = [&](const unsigned char* base, int r) __attribute__((always_inline)) -> v8i_t {
+    const v4i p0 = *reinterpret_cast<const v4i*>(base + r * EBK + 16 * (g ^ (r & 7)));
+    const v4i p1 = *reinterpret_cast<const v4i*>(base + r * EBK + 16 * ((4 + g) ^ (r & 7)));
+    return v8i_t{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+  };
+
+  if (KS > 0) issue(0);
+  for (int ks = 0; ks < KS; ++ks) {
+    wait_vmcnt<0>();   // step ks has landed
+    lds_barrier();     // ... for every wave; step ks-1's slot is free
+    issue(ks + 1);
+    const unsigned char* slot = smem + (ks % E2_STAGES) * E2_STAGE;
+    const unsigned char* rec = slot + E2_SC_OFF + w * 256;
+    v8i_t bf[4];
+    int sb_b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf[j] = frag(slot + E2_OPND_BYTES, wn * 64 + 16 * j + lo);
+      sb_b[j] = rec[32 + 4 * (2 * wn + (j >> 1)) + g];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const v8i_t af = frag(slot, wm * 128 + 16 * i + lo);
+      const int sa_b = rec[4 * (4 * wm + (i >> 1)) + g];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sb_b[j], 0,
+                                                                       sa_b);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue: lane holds row 16i + (lane & 15), columns 16j + 4g .. +3
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = row0 + wm * 128 + 16 * i + lo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t col = col0 + wn * 64 + 16 * j + 4 * g;
@@ -261,8 +391,11 @@ hipError_t set_gemm_e8m0_attributes() {
   hipError_t e = hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      2 * E_STAGE);
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             3 * E_STAGE);
+  e = hipFuncSetAttribute((const void*)gemm_e8m0_nt_kernel<3>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          3 * E_STAGE);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_e8m0_nt_big_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             E2_STAGES * E2_STAGE);
 }
 
 hipError_t launch_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, const void* ebt, void* c, int64_t M,
@@ -290,6 +423,15 @@ hipError_t launch_gemm_e8m0_nt(const void* a, const void* ea, const void* bt, co
       E8_SMALLM(4, 4);
     }
 #undef E8_SMALLM
+    return hipGetLastError();
+  }
+  const int64_t big_m = (M + EB2M - 1) / EB2M, big_n = (N + EB2N - 1) / EB2N;
+  if (big_m * big_n >= E_BIG_TILES) {
+    // XCD-aware tile order (as in the exact GEMM) when the tile count allows it
+    const int remap = (big_m * big_n) % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL(gemm_e8m0_nt_big_kernel, dim3((unsigned)(big_m * big_n)), dim3(E2THREADS),
+                       E2_STAGES * E2_STAGE, stream, (const uint8_t*)a, (const uint8_t*)ea, (const uint8_t*)bt,
+                       (const uint8_t*)ebt, (uint16_t*)c, M, N, K, big_n, remap);
     return hipGetLastError();
   }
   const int64_t tiles_m = (M + EBM - 1) / EBM, tiles_n = (N + EBN - 1) / EBN;

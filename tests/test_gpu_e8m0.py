@@ -180,6 +180,23 @@ def test_gemm_e8m0_ring_depth_switch_keeps_rows():
     assert np.array_equal(part, full[:128])
 
 
+@pytest.mark.parametrize("M,N", [(4096, 4096), (4100, 4128)])
+def test_gemm_e8m0_big_tile_rows_equal_small_tile_rows(M, N):
+    """A grid of at least 256 tiles of 256 x 256 runs the 256 x 256 kernel
+    (eight 128 x 64 wave tiles; XCD-remapped at 4096 x 4096, ragged in both
+    dimensions at 4100 x 4128).  128-row slices of the same operands run the
+    128 x 128 kernel, and the last 4 rows the small-M kernel: every row is
+    bitwise the same."""
+    qa, ea, qbt, ebt = _operands(8800 + M, M, N, 256)
+    say(f"gemm_e8m0 256 x 256 tiles {M} x {N}")
+    full = gpu_gemm_e8m0(qa, ea, qbt, ebt)
+    for r0 in (0, 1920, M - (M % 128 or 128)):
+        r1 = min(r0 + 128, M)
+        say(f"gemm_e8m0 rows {r0}..{r1} alone")
+        part = gpu_gemm_e8m0(qa[r0:r1], ea[r0 // 32:-(-r1 // 32)], qbt, ebt)
+        assert np.array_equal(part, full[r0:r1]), (M, N, r0)
+
+
 @pytest.mark.parametrize("K", [128, 896, 1152, 4096])
 def test_gemm_e8m0_small_m_rows_equal_tile_rows(K):
     """M <= 64 at this width runs the small-M kernel (a register ring of
