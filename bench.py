@@ -340,6 +340,18 @@ def main():
         pc_us[mode] = med * 1e3
     promote_ceiling_tflops = (pc_wg * 8 * pc_iters * 8 * probe.PROMOTE_CEILING_FLOPS_PER_STEP
                               / (pc_us[0] * 1e-6) / 1e12)
+    # the same mix at two waves per SIMD (the tile kernel's occupancy): the
+    # interleaved loop, then bursts of 2, 3, 4 and 6 MFMAs each followed by the
+    # previous burst's FMAs; reported in nanoseconds per step and SIMD
+    pc2_wg, pc2_steps = 256, 48000
+    pc2_ns = {}
+    for mode in (0, 4, 5, 6, 7):
+        it = pc2_steps // probe.PROMOTE_STEPS_PER_ITER[mode]
+        pc2_out = pc_out[:pc2_wg * 8]
+        probe.promote_ceiling(pc2_out, pc2_wg, 200, mode)
+        med, _, _ = time_launch(lambda mode=mode, it=it: probe.promote_ceiling(pc2_out, pc2_wg, it, mode), 5,
+                                do_flush=False)
+        pc2_ns[mode] = med * 1e6 / (pc2_wg * 8 * pc2_steps / 1024)
 
     for _ in range(5):
         gemm_only()
@@ -364,7 +376,12 @@ def main():
                             "what": "registers-only loop of one 16x16x32 bf16 MFMA + four fp32 FMAs per step, "
                                     "512 workgroups of eight waves (4 waves per SIMD); also the same "
                                     "steps with the MFMAs alone, with the FMAs alone, and with the FP8 form of "
-                                    "the MFMA alone"},
+                                    "the MFMA alone",
+                            "two_waves_per_simd_ns_per_step": {
+                                "interleaved": round(pc2_ns[0], 3),
+                                **{f"bursts_of_{probe.PROMOTE_BURSTS[m]}": round(pc2_ns[m], 3) for m in (4, 5, 6, 7)}},
+                            "two_waves_what": "256 workgroups of eight waves; nanoseconds per step and SIMD "
+                                              "(times the shader clock: cycles per step)"},
     }
 
     # square 256^3 (quantize both operands + GEMM, and the GEMM alone): a

@@ -410,21 +410,28 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     }
 
     // 32 sub-tile partials, j outer, so that each B fragment is dead after its
-    // four uses and is refilled with the next K-block's; partials pass through
-    // a ring of PDEPTH partials so PDEPTH MFMAs are in flight while the VALU
-    // promotes the oldest.  The staging of K-block kb+2 (decode + LDS stores)
-    // is cut into four pieces spread over the MFMA sequence, so that no stretch
-    // of the iteration is conversions alone.
+    // four uses and is refilled with the next K-block's.  The MFMAs run in
+    // bursts of BU, each followed by the promotions of the burst before it, so
+    // partials pass through a ring of 2 BU.  A SIMD runs two waves of the
+    // tile, and a burst of MFMAs from one overlaps a burst of fmas from the
+    // other: a register-only loop of this mix at two waves per SIMD took 32.4
+    // cycles per MFMA with its four fmas one MFMA apart, 29.4 in bursts of two
+    // and 28.1 in bursts of three (bursts of four need eight partials, which
+    // spill here).  The staging of K-block kb+3 (decode + LDS stores) is cut
+    // into four pieces spread over the MFMA sequence, so that no stretch of
+    // the iteration is conversions alone.
     //
     // Wave priority falls in steps over the iteration (3 at its start, 0 from
-    // the 30th of 38 steps on; proportionally in a light tile).  A SIMD runs two waves of the tile; at equal priority
-    // the older one issues first, runs ahead, and then waits at the barrier
-    // while the other finishes alone.  Measured with per-wave cycle counters
-    // at 4096^3: the leading waves waited 706 cycles per K-block at the
-    // barrier, the others 106, in 2330-cycle K-blocks.  With the priority
-    // steps the wave that is behind in the iteration issues first, the two
-    // stay close, and the kernel took 139 us against 145.
-    constexpr int PDEPTH = 6;
+    // the 30th of 32 MFMAs on; proportionally in a light tile).  At equal
+    // priority the older wave of a SIMD issues first, runs ahead, and then
+    // waits at the barrier while the other finishes alone.  Measured with
+    // per-wave cycle counters at 4096^3: the leading waves waited 706 cycles
+    // per K-block at the barrier, the others 106, in 2330-cycle K-blocks.
+    // With the priority steps the wave that is behind in the iteration issues
+    // first, the two stay close, and the kernel took 139 us against 145.
+    constexpr int BU = 3;
+    constexpr int PDEPTH = 2 * BU;
+    constexpr int NG = (NQ + BU - 1) / BU;
     v4f pr[PDEPTH];
     if constexpr (!COMPUTE) {
       store_stage(sf, ra, rb);
@@ -434,44 +441,47 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     constexpr int QS0 = NQ * 4 / 32, QS1 = NQ * 10 / 32, QS2 = NQ * 16 / 32, QS3 = NQ * 22 / 32;  // staging
     if constexpr (COMPUTE) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-    for (int q = 0; q < (COMPUTE ? NQ + PDEPTH : 0); ++q) {
-      if (q == QP2) __builtin_amdgcn_s_setprio(2);
-      if (q == QP1) __builtin_amdgcn_s_setprio(1);
-      if (q == QP0) __builtin_amdgcn_s_setprio(0);
-      if (q >= PDEPTH) {
-        const int u = q - PDEPTH;
-        const int ui = u & 3, uj = u >> 2;
-        if constexpr (TG) {
-          if ((u & 7) == 0) s4 = sa4 * sbs[uj >> 1];  // this column block's four row scales
-          promote(acc[ui][uj], pr[u % PDEPTH], s4[ui]);
-        } else {
-          promote(acc[ui][uj], pr[u % PDEPTH], s_cur[ui >> 1][uj >> 1]);
-        }
-      }
-      if (q < NQ) {
+    for (int g = 0; g < (COMPUTE ? NG + 1 : 0); ++g) {
+#pragma unroll
+      for (int q = g * BU; q < (g + 1) * BU; ++q) {
+        if (q >= NQ) break;
+        if (q == QP2) __builtin_amdgcn_s_setprio(2);
+        if (q == QP1) __builtin_amdgcn_s_setprio(1);
+        if (q == QP0) __builtin_amdgcn_s_setprio(0);
         const int qi = q & 3, qj = q >> 2;
         pr[q % PDEPTH] = TG ? mfma_partial(bfrag[qj], af[qi]) : mfma_partial(af[qi], bfrag[qj]);
         if (qi == 3) bfrag[qj] = read_b(sn, qj);   // last use of this B fragment
         if (qj == JN - 1) af[qi] = read_a(sn, qi);  // last use of this A fragment
+        // Unconditional (clamped) staging: a branch here would keep the old
+        // and new register contents alive together.  Past the end the stage
+        // written is never read.  Each register is reloaded (K-block kb+5) as
+        // soon as both of its halves are staged, A before B as in the prologue.
+        if (q == QS0) store_piece(sf, 0, ra, rb);
+        if (q == QS1) {
+          store_piece(sf, 1, ra, rb);
+          load_a_only(kb + 5 < KB ? kb + 5 : KB - 1, ra);
+        }
+        if (q == QS2) store_piece(sf, 2, ra, rb);
+        if (q == QS3) {
+          store_piece(sf, 3, ra, rb);
+          load_b_only(kb + 5 < KB ? kb + 5 : KB - 1, rb);
+        }
       }
-      // Unconditional (clamped) staging: a branch here would keep the old and
-      // new register contents alive together.  Past the end the stage written
-      // is never read.  Each register is reloaded (K-block kb+4) as soon as
-      // both of its halves are staged, A before B as in the prologue.
-      if (q == QS0) store_piece(sf, 0, ra, rb);
-      if (q == QS1) {
-        store_piece(sf, 1, ra, rb);
-        load_a_only(kb + 5 < KB ? kb + 5 : KB - 1, ra);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g >= 1) {
+#pragma unroll
+        for (int u = (g - 1) * BU; u < g * BU; ++u) {
+          if (u >= NQ) break;
+          const int ui = u & 3, uj = u >> 2;
+          if constexpr (TG) {
+            if ((u & 7) == 0) s4 = sa4 * sbs[uj >> 1];  // this column block's four row scales
+            promote(acc[ui][uj], pr[u % PDEPTH], s4[ui]);
+          } else {
+            promote(acc[ui][uj], pr[u % PDEPTH], s_cur[ui >> 1][uj >> 1]);
+          }
+        }
       }
-      if (q == QS2) store_piece(sf, 2, ra, rb);
-      if (q == QS3) {
-        store_piece(sf, 3, ra, rb);
-        load_b_only(kb + 5 < KB ? kb + 5 : KB - 1, rb);
-      }
-      // scheduling groups of three MFMAs: every promotion in a group reads a
-      // partial formed at least one group earlier, so the compiler never has
-      // to place an fma right behind the MFMA it depends on
-      if (q % 3 == 2) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (COMPUTE) {
       if constexpr (TG) read_tg_scales(kb + 1, sa4, sbs);

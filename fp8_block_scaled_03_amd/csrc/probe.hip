@@ -169,6 +169,56 @@ __global__ void __launch_bounds__(512) probe_promote_ceiling_kernel(float* __res
   if (lane == 0) out[(int64_t)blockIdx.x * 8 + (threadIdx.x >> 6)] = t;
 }
 
+// The same mix issued in bursts: BU MFMAs back to back, then the 4 BU FMAs
+// that promote the previous burst's partials (a ring of 2 BU partials), 12
+// steps per iteration (every BU used divides 12), iterations in pairs so that
+// the two halves of the ring swap roles without register copies.  With two
+// waves on a SIMD, the MFMA burst of one can overlap the FMA burst of the
+// other.
+template <int BU>
+__global__ void __launch_bounds__(512) probe_promote_burst_kernel(float* __restrict__ out, int iters, float seed) {
+  constexpr int H = 12;
+  static_assert(H % BU == 0, "burst size divides the iteration");
+  const int lane = threadIdx.x & 63;
+  v8bf a[H], b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int u = 0; u < H; ++u) a[u][e] = (__bf16)(seed * (float)(lane + e + 3 * u + 1));
+    b[e] = (__bf16)(seed * (float)(lane - e + 3));
+  }
+  v4f acc[4], r0[H], r1[H];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < H; ++i) r0[i] = r1[i] = v4f{seed, seed, seed, seed};
+  float s = seed;
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      v4f* older = half == 0 ? r0 : r1;  // partials promoted in this iteration
+      v4f* newer = half == 0 ? r1 : r0;  // partials formed in this iteration
+#pragma unroll
+      for (int h = 0; h < H; h += BU) {
+#pragma unroll
+        for (int u = 0; u < BU; ++u) newer[h + u] = mfma_partial(a[h + u], b);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < BU; ++u) promote(acc[(h + u) & 3], older[h + u], s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s = s * 0.999f;
+      b = __builtin_shufflevector(b, b, 1, 2, 3, 4, 5, 6, 7, 0);
+    }
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+#pragma unroll
+  for (int i = 0; i < H; ++i) t += r0[i][0] + r0[i][1] + r0[i][2] + r0[i][3] + r1[i][0] + r1[i][1] + r1[i][2] + r1[i][3];
+  if (lane == 0) out[(int64_t)blockIdx.x * 8 + (threadIdx.x >> 6)] = t;
+}
+
 // Streaming read of `n16` 16-byte words: every thread reads a grid-strided
 // sequence, eight loads in flight, and folds them with xor; one word per wave
 // is written so that nothing is dead.
@@ -226,16 +276,21 @@ int fp8bs_probe_mfma_scale(const void* a, const void* bt, const void* ea, const 
 
 int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode, void* stream) {
   if (!out) return 1;
-  if (workgroups <= 0 || iters <= 0 || mode < 0 || mode > 3) return 2;
+  if (workgroups <= 0 || iters <= 0 || mode < 0 || mode > 7) return 2;
+  if (mode >= 4 && (iters & 1)) return 2;
   const dim3 grid((unsigned)workgroups), block(512);
-  if (mode == 0)
-    hipLaunchKernelGGL(probe_promote_ceiling_kernel<0>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
-  else if (mode == 1)
-    hipLaunchKernelGGL(probe_promote_ceiling_kernel<1>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
-  else if (mode == 2)
-    hipLaunchKernelGGL(probe_promote_ceiling_kernel<2>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
-  else
-    hipLaunchKernelGGL(probe_promote_ceiling_kernel<3>, grid, block, 0, (hipStream_t)stream, out, iters, 1.0f / 1024.0f);
+  const hipStream_t st = (hipStream_t)stream;
+  const float seed = 1.0f / 1024.0f;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(probe_promote_ceiling_kernel<0>, grid, block, 0, st, out, iters, seed); break;
+    case 1: hipLaunchKernelGGL(probe_promote_ceiling_kernel<1>, grid, block, 0, st, out, iters, seed); break;
+    case 2: hipLaunchKernelGGL(probe_promote_ceiling_kernel<2>, grid, block, 0, st, out, iters, seed); break;
+    case 3: hipLaunchKernelGGL(probe_promote_ceiling_kernel<3>, grid, block, 0, st, out, iters, seed); break;
+    case 4: hipLaunchKernelGGL(probe_promote_burst_kernel<2>, grid, block, 0, st, out, iters, seed); break;
+    case 5: hipLaunchKernelGGL(probe_promote_burst_kernel<3>, grid, block, 0, st, out, iters, seed); break;
+    case 6: hipLaunchKernelGGL(probe_promote_burst_kernel<4>, grid, block, 0, st, out, iters, seed); break;
+    default: hipLaunchKernelGGL(probe_promote_burst_kernel<6>, grid, block, 0, st, out, iters, seed); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -61,9 +61,11 @@ int fp8bs_probe_mfma_scale(const void* a, const void* bt, const void* ea, const 
  * with non-packed fp32 FMAs.  mode 0: that mix; mode 1: the MFMAs alone;
  * mode 2: the FMAs alone (the same counts), so that the three rates show how
  * far the two kinds of work overlap; mode 3: v_mfma_f32_16x16x32_fp8_fp8
- * alone, the FP8 form of the same partial.  out [workgroups * 8] fp32 (one
- * value per wave, written so that nothing is dead code).  workgroups,
- * iters > 0, mode in 0..3.
+ * alone, the FP8 form of the same partial.  Modes 4-7 run the mix in bursts
+ * of 2, 3, 4 and 6 MFMAs, each followed by the FMAs that promote the previous
+ * burst's partials, `iters` x 12 steps (iters even).  out [workgroups * 8]
+ * fp32 (one value per wave, written so that nothing is dead code).
+ * workgroups, iters > 0, mode in 0..7; 2 for any other value.
  */
 int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode, void* stream);
 
