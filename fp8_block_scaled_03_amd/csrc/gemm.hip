@@ -947,16 +947,32 @@ __global__ void __launch_bounds__(STHREADS) gemm_smallm_kernel(const uint8_t* __
         sbv[q] = rec[16 + q * NCB + own_cb];
       }
     }
+    // K-block q's partials are promoted after K-block q+1's MFMAs are issued,
+    // so no fma waits on the MFMA right before it; each acc[t] still takes the
+    // K-blocks in ascending order (the same bits).  Measured at K = 8192:
+    // N = 28672, M = 32 / 48 / 64 62.1 / 82.5 / 104.9 -> 60.1 / 77.9 / 97.3 us,
+    // M <= 16 unchanged.  (The K-major kernel measured slower this way at
+    // M = 64, N = 28672: 93.8 against 86.7 us.)
+    v4f pp[2][Cfg::TPW];
+    float psc[2][Cfg::TPW];
 #pragma unroll
-    for (int q = 0; q < SWAVES; ++q) {
-      const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
+    for (int q = 0; q <= SWAVES; ++q) {
+      if (q < SWAVES) {
+        const v8bf bfrag = e4m3x8_to_bf16x8(braw[q]);
 #pragma unroll
-      for (int t = 0; t < Cfg::TPW; ++t) {
-        const v8bf afrag = Cfg::A_SHARED ? abf[q][t] : e4m3x8_to_bf16x8(araw[q][t]);
-        const v4f p = TG ? mfma_partial(bfrag, afrag) : mfma_partial(afrag, bfrag);
-        const float sc = (TG ? sat[q][t] : sav[q][tile_of(t) >> 1]) * sbv[q];
-        if (FULL || q < nkb) promote(acc[t], p, sc);
+        for (int t = 0; t < Cfg::TPW; ++t) {
+          const v8bf afrag = Cfg::A_SHARED ? abf[q][t] : e4m3x8_to_bf16x8(araw[q][t]);
+          pp[q & 1][t] = TG ? mfma_partial(bfrag, afrag) : mfma_partial(afrag, bfrag);
+          psc[q & 1][t] = (TG ? sat[q][t] : sav[q][tile_of(t) >> 1]) * sbv[q];
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (q > 0) {
+#pragma unroll
+        for (int t = 0; t < Cfg::TPW; ++t)
+          if (FULL || q - 1 < nkb) promote(acc[t], pp[(q - 1) & 1][t], psc[(q - 1) & 1][t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
