@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(const uint16_t* __restric
                                   sat448(quotient(bf16_hi(ws[2 * i + 1]), FAST_)));
         if (ok[k]) {
           const int64_t row = rb * 32 + 4 * k + rsub;
-          *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
+          store_codes8(q + row * cols + col, packed[0], packed[1]);
         }
       }
     };
@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(256) quantize_tg_kernel(const uint16_t* __rest
                                   sat448(quotient(bf16_hi(ws[2 * i + 1]), k, FAST_)));
         if (ok[k]) {
           const int64_t row = rb * 32 + 4 * k + rsub;
-          *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
+          store_codes8(q + row * cols + col, packed[0], packed[1]);
           if (cpart == 0) scales[row * cb_count + cb] = sk[k];
         }
       }
@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(256) quantize_e8m0_kernel(const uint16_t* __re
                                 sat448(bf16_lo(ws[2 * i + 1]) * r), sat448(bf16_hi(ws[2 * i + 1]) * r));
       if (ok[k]) {
         const int64_t row = rb * 32 + 4 * k + rsub;
-        *reinterpret_cast<uint2*>(q + row * cols + col) = make_uint2(packed[0], packed[1]);
+        store_codes8(q + row * cols + col, packed[0], packed[1]);
       }
     }
     if (cpart == 0 && rsub == 0 && cb_ok) e8[rb * cb_count + cb] = (uint8_t)(E + 127);
