@@ -352,6 +352,11 @@ def main():
         med, _, _ = time_launch(lambda mode=mode, it=it: probe.promote_ceiling(pc2_out, pc2_wg, it, mode), 5,
                                 do_flush=False)
         pc2_ns[mode] = med * 1e6 / (pc2_wg * 8 * pc2_steps / 1024)
+    # the hardware-scaled f8f6f4 MFMA alone (the power-of-two-scale contract's
+    # instruction), 512 workgroups of eight waves
+    probe.promote_ceiling(pc_out, pc_wg, 200, 8)
+    sm_med, _, _ = time_launch(lambda: probe.promote_ceiling(pc_out, pc_wg, pc_iters, 8), 5, do_flush=False)
+    scaled_mfma_tflops = pc_wg * 8 * pc_iters * 8 * probe.SCALED_MFMA_FLOPS / (sm_med * 1e-3) / 1e12
 
     for _ in range(5):
         gemm_only()
@@ -381,7 +386,8 @@ def main():
                                 "interleaved": round(pc2_ns[0], 3),
                                 **{f"bursts_of_{probe.PROMOTE_BURSTS[m]}": round(pc2_ns[m], 3) for m in (4, 5, 6, 7)}},
                             "two_waves_what": "256 workgroups of eight waves; nanoseconds per step and SIMD "
-                                              "(times the shader clock: cycles per step)"},
+                                              "(times the shader clock: cycles per step)",
+                            "scaled_fp8_mfma_only_tflops": round(scaled_mfma_tflops, 1)},
     }
 
     # square 256^3 (quantize both operands + GEMM, and the GEMM alone): a
@@ -536,6 +542,7 @@ def main():
         e_med, e_min, _ = time_launch(efn, reps)
         e8["gemm_e8m0_4096_ms"] = ms_entry(e_med, e_min)
         e8["gemm_e8m0_4096_tflops_median"] = round(gemm_flops / (e_med * 1e-3) / 1e12, 1)
+        e8["gemm_e8m0_4096_frac_of_scaled_mfma_loop"] = round(gemm_flops / (e_med * 1e-3) / 1e12 / scaled_mfma_tflops, 4)
         del eqa, eea, eqb, eeb
         pwl = W.prefill(28672)
         pqa, pea = fp8bs.quantize_e8m0(to_dev_bf16(pwl.a_bits()))

@@ -219,6 +219,34 @@ __global__ void __launch_bounds__(512) probe_promote_burst_kernel(float* __restr
   if (lane == 0) out[(int64_t)blockIdx.x * 8 + (threadIdx.x >> 6)] = t;
 }
 
+// The hardware-scaled MFMA alone: v_mfma_scale_f32_16x16x128_f8f6f4 on E4M3
+// operands with unit scales (E8M0 127), eight accumulators, `iters` x 8
+// instructions per wave; the rate the power-of-two-scale GEMM can reach.
+__global__ void __launch_bounds__(512) probe_scaled_mfma_kernel(float* __restrict__ out, int iters, float seed) {
+  const int lane = threadIdx.x & 63;
+  const int bits = (int)(seed * 1024.0f);
+  v8i_t a[4], b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u][e] = 0x38383838 + bits * (lane + e + u);
+    b[e] = 0x30303030 + bits * (lane - e);
+  }
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u & 3], b, acc[u], 0, 0, 0, 127, 0, 127);
+    b = __builtin_shufflevector(b, b, 1, 2, 3, 4, 5, 6, 7, 0);
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  if (lane == 0) out[(int64_t)blockIdx.x * 8 + (threadIdx.x >> 6)] = t;
+}
+
 // Streaming read of `n16` 16-byte words: every thread reads a grid-strided
 // sequence, eight loads in flight, and folds them with xor; one word per wave
 // is written so that nothing is dead.
@@ -276,8 +304,8 @@ int fp8bs_probe_mfma_scale(const void* a, const void* bt, const void* ea, const 
 
 int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode, void* stream) {
   if (!out) return 1;
-  if (workgroups <= 0 || iters <= 0 || mode < 0 || mode > 7) return 2;
-  if (mode >= 4 && (iters & 1)) return 2;
+  if (workgroups <= 0 || iters <= 0 || mode < 0 || mode > 8) return 2;
+  if (mode >= 4 && mode <= 7 && (iters & 1)) return 2;
   const dim3 grid((unsigned)workgroups), block(512);
   const hipStream_t st = (hipStream_t)stream;
   const float seed = 1.0f / 1024.0f;
@@ -289,7 +317,8 @@ int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode,
     case 4: hipLaunchKernelGGL(probe_promote_burst_kernel<2>, grid, block, 0, st, out, iters, seed); break;
     case 5: hipLaunchKernelGGL(probe_promote_burst_kernel<3>, grid, block, 0, st, out, iters, seed); break;
     case 6: hipLaunchKernelGGL(probe_promote_burst_kernel<4>, grid, block, 0, st, out, iters, seed); break;
-    default: hipLaunchKernelGGL(probe_promote_burst_kernel<6>, grid, block, 0, st, out, iters, seed); break;
+    case 7: hipLaunchKernelGGL(probe_promote_burst_kernel<6>, grid, block, 0, st, out, iters, seed); break;
+    default: hipLaunchKernelGGL(probe_scaled_mfma_kernel, grid, block, 0, st, out, iters, seed); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }

@@ -82,7 +82,8 @@ def promote_ceiling(out, workgroups: int, iters: int, mode: int = 0):
     mode 0 = MFMA + four FMAs per step, 1 = the MFMAs alone, 2 = the FMAs alone,
     3 = the FP8 form of the MFMA alone (iters x 8 steps); 4-7 = the mix in
     bursts of PROMOTE_BURSTS[mode] MFMAs, each followed by the previous burst's
-    FMAs (iters x 12 steps, iters even)."""
+    FMAs (iters x 12 steps, iters even); 8 = the hardware-scaled f8f6f4 MFMA
+    alone (iters x 8 instructions of SCALED_MFMA_FLOPS each)."""
     rc = load_probe_library().fp8bs_probe_promote_ceiling(
         _dev(out, torch.float32, (workgroups * 8,), "out"), workgroups, iters, mode, _stream_ptr(out))
     _ok(rc, "fp8bs_probe_promote_ceiling")
@@ -90,7 +91,8 @@ def promote_ceiling(out, workgroups: int, iters: int, mode: int = 0):
 
 PROMOTE_CEILING_FLOPS_PER_STEP = 2 * 16 * 16 * 32   # one 16x16x32 MFMA
 PROMOTE_BURSTS = {4: 2, 5: 3, 6: 4, 7: 6}             # burst modes -> MFMAs per burst
-PROMOTE_STEPS_PER_ITER = {0: 8, 1: 8, 2: 8, 3: 8, 4: 12, 5: 12, 6: 12, 7: 12}
+PROMOTE_STEPS_PER_ITER = {0: 8, 1: 8, 2: 8, 3: 8, 4: 12, 5: 12, 6: 12, 7: 12, 8: 8}
+SCALED_MFMA_FLOPS = 2 * 16 * 16 * 128              # one 16x16x128 scaled MFMA
 
 
 def stream_read(buf, out, workgroups: int):

@@ -63,9 +63,12 @@ int fp8bs_probe_mfma_scale(const void* a, const void* bt, const void* ea, const 
  * far the two kinds of work overlap; mode 3: v_mfma_f32_16x16x32_fp8_fp8
  * alone, the FP8 form of the same partial.  Modes 4-7 run the mix in bursts
  * of 2, 3, 4 and 6 MFMAs, each followed by the FMAs that promote the previous
- * burst's partials, `iters` x 12 steps (iters even).  out [workgroups * 8]
- * fp32 (one value per wave, written so that nothing is dead code).
- * workgroups, iters > 0, mode in 0..7; 2 for any other value.
+ * burst's partials, `iters` x 12 steps (iters even).  Mode 8 runs
+ * v_mfma_scale_f32_16x16x128_f8f6f4 alone on E4M3 operands with unit
+ * scales (65536 flops each), `iters` x 8 instructions per wave: the rate of
+ * the power-of-two-scale contract.  out [workgroups * 8] fp32 (one value per
+ * wave, written so that nothing is dead code).  workgroups, iters > 0, mode
+ * in 0..8; 2 for any other value.
  */
 int fp8bs_probe_promote_ceiling(float* out, int workgroups, int iters, int mode, void* stream);
 

@@ -46,7 +46,7 @@ def test_probe_library_exports_every_declared_symbol_and_checks_arguments():
     assert lib.fp8bs_probe_mfma_scale(A16, A16, A16, A16, A4, A4, 0, None) == 2
     assert lib.fp8bs_probe_promote_ceiling(None, 1, 1, 0, None) == 1
     assert lib.fp8bs_probe_promote_ceiling(A4, 1, 1, 4, None) == 2                        # burst mode, odd iters
-    assert lib.fp8bs_probe_promote_ceiling(A4, 1, 2, 8, None) == 2                        # no mode 8
+    assert lib.fp8bs_probe_promote_ceiling(A4, 1, 2, 9, None) == 2                        # no mode 9
     assert lib.fp8bs_probe_stream_read(A16, 24, A4, 1, None) == 2                          # bytes % 16
 
 
