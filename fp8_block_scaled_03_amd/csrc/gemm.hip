@@ -414,10 +414,11 @@ __device__ __forceinline__ void tile_body(const TileArgs& p, unsigned char* smem
     // bursts of BU, each followed by the promotions of the burst before it, so
     // partials pass through a ring of 2 BU.  A SIMD runs two waves of the
     // tile, and a burst of MFMAs from one overlaps a burst of fmas from the
-    // other: a register-only loop of this mix at two waves per SIMD took 32.4
-    // cycles per MFMA with its four fmas one MFMA apart, 29.4 in bursts of two
-    // and 28.1 in bursts of three (bursts of four need eight partials, which
-    // spill here).  The staging of K-block kb+3 (decode + LDS stores) is cut
+    // other: the probe's register-only loop of this mix at two waves per SIMD
+    // took 26.6 cycles per MFMA and its four fmas interleaved, 24.6 in bursts
+    // of two or three and 23.3 in bursts of six (bursts of four or more need
+    // eight or more partials, which spill here; in this kernel bursts of
+    // three beat bursts of two).  The staging of K-block kb+3 (decode + LDS stores) is cut
     // into four pieces spread over the MFMA sequence, so that no stretch of
     // the iteration is conversions alone.
     //
