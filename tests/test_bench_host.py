@@ -1,4 +1,6 @@
-"""Host-side helpers of bench.py (no GPU): the shader-clock table parser."""
+"""Host-side parts of bench.py (no GPU): the shader-clock table parser, the
+check that the committed counter summaries match the sources, and the
+refusal of runs on more than one GPU."""
 
 import importlib.util
 import os
@@ -43,3 +45,20 @@ def test_committed_counter_summaries_match_current_sources():
                     fields[k.strip()] = v.strip()
         sources = fields.get("sources", " ".join(profiling.GEMM_SOURCES)).split()
         assert fields.get("source_sha") == profiling.source_sha(sources), os.path.basename(path)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench measures one GPU's share; any other --gpus (or a launcher's
+    WORLD_SIZE above 1) ends with a message and status 2 before any GPU work."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("WORLD_SIZE", None)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, env=env, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    env["WORLD_SIZE"] = "4"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert r.returncode == 2
