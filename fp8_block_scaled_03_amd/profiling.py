@@ -36,10 +36,12 @@ def _code_only(text: str) -> str:
 
 def source_sha(paths=GEMM_SOURCES) -> str:
     """Hash of the listed sources (code only) and of the compiler flags every
-    HIP source is built with: a change to either retires a profile."""
+    HIP source is built with: a change to either retires a profile.  Include
+    paths are left out: they name the checkout's location, which differs
+    between the machine that writes a summary and the one that reads it."""
     from . import build
     h = hashlib.sha256()
-    h.update(" ".join(build.COMMON_FLAGS).encode())
+    h.update(" ".join(f for f in build.COMMON_FLAGS if not f.startswith("-I")).encode())
     for p in paths:
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
