@@ -54,6 +54,12 @@ FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s
 BF16_DENSE_PEAK_TFLOPS = 2500.0
 METRIC = "FP8 block-scaled GEMM TFLOPS & % MFMA peak @4096³; small-M HBM GB/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_tile_square4096.txt")
+# An idle MI355X runs its first few hundred steps at a lower shader clock
+# (measured with 20 timed steps: 676 TFLOP/s after 5 warm-up steps, 766 after
+# 50, 804 after 100, 849 after 300).  Before the requested warm-up steps the
+# step therefore runs, untimed, for at least this long, so that the timed
+# steps measure the sustained rate whatever --warmup is.
+PREWARM_SECONDS = 0.5
 
 
 def parse():
@@ -254,6 +260,14 @@ def main():
         fp8bs.gemm(qa, sa, qb, sb, out=c)
         ev[i][1].record(stream)
 
+    prewarm_steps = 0
+    t_pw = time.perf_counter()
+    while time.perf_counter() - t_pw < PREWARM_SECONDS:
+        for _ in range(20):
+            step()
+        prewarm_steps += 20
+        torch.cuda.synchronize()
+    prewarm_s = time.perf_counter() - t_pw
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -302,6 +316,8 @@ def main():
         "config": {"workload": "square-4096: quantize A, B (bf16 -> E4M3, 32x32 scales) + block-scaled GEMM",
                    "M": M, "N": N, "K": K, "block": 32, "seed": wl.seed},
         "roofline": roofline,
+        "prewarm": {"steps": prewarm_steps, "seconds": round(prewarm_s, 3),
+                    "what": "untimed steps run before the warm-up steps until the GPU holds its sustained clock"},
     }
     if args.roofline_only:
         print(json.dumps(out), flush=True)
